@@ -1,0 +1,259 @@
+"""Benchmark of the NVFP4 W4A4 MoE hot path on one MI355X.
+
+One step = one pass of the whole path over a Qwen3-30B-A3B-shaped layer at
+4096 tokens (hidden 2048, 128 experts, top-8, expert intermediate 768):
+  dense W4A4 QKV (quantise rows, one-group GEMM N=5120)
+  -> MoE forward: route + permute + quantise, gate_up grouped GEMM (N=1536),
+     weighted SwiGLU + quantise, down grouped GEMM (N=2048), combine
+  -> BF16 dgrad: gather dY, grouped GEMM with W_d, SwiGLU backward, grouped
+     GEMM with W_gu, combine.
+Inputs (activations with 1% x20 outliers, softmax top-8 routing of N(0,1)
+logits, N(0, 0.02) weights, N(0,1) dY) are synthetic and seeded, resident in
+HBM before timing; weights are quantised to NVFP4 once before timing.
+
+Prints one JSON line.  `value` is the W4A4 grouped-GEMM throughput (gate_up +
+down FLOPs over their device time, HIP events on the launch stream); the
+quantize-permute GB/s, every op's time and roofline fraction, the dominant
+kernel's roofline object and the CPU oracle's throughput are in the same line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+PEAK_F16_TFLOPS = 2500.0     # MI355X dense FP16/BF16 MFMA
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--routing", default="softmax", choices=["softmax", "uniform", "zipf"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle sample's CPU time")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import precision_moe_gemm_amd as pmg
+    import workloads as W
+
+    if not os.path.exists(pmg.library_path()):
+        from precision_moe_gemm_amd import build
+        build.build_library()
+    pmg.load_library()
+    dev = torch.device("cuda:0")
+    S = W.LayerShape()
+    T, H, E, k, I, R = S.T, S.H, S.E, S.k, S.I, S.R
+    cfg = W.CFG_LAYER
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # ---------------- inputs (host synthesis, then resident on the device)
+    t0 = time.time()
+    x_bits = W.activations(T, H, config=cfg)
+    ids_np, tw_np = W.make_routing(args.routing, T, E, k, cfg)
+    wgu_bits, wd_bits = W.moe_weights_bf16(S, cfg)
+    wqkv_bits = W.qkv_weight_bf16(S, cfg)
+    dy_bits = W.grad_output_bf16(S, cfg)
+    x, dy = bf16(x_bits), bf16(dy_bits)
+    ids = torch.from_numpy(ids_np).to(dev)
+    tw = torch.from_numpy(tw_np.reshape(-1)).to(dev)
+    wgu, wd, wqkv = bf16(wgu_bits), bf16(wd_bits), bf16(wqkv_bits)
+    # NVFP4 weights (quantised once; per output row FP32 scale)
+    q_gu = [t.view(E, 2 * I, -1) if t.dim() == 2 else t.view(E, 2 * I)
+            for t in pmg.nvfp4_quantize_rows(wgu.view(E * 2 * I, H))]
+    q_d = [t.view(E, H, -1) if t.dim() == 2 else t.view(E, H)
+           for t in pmg.nvfp4_quantize_rows(wd.view(E * H, I))]
+    q_qkv = [t.unsqueeze(0) for t in pmg.nvfp4_quantize_rows(wqkv)]
+    qkv_off = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    # outputs / intermediates
+    ws = torch.empty(pmg.permute_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
+    a_qkv = {"c": torch.empty(T, H // 2, dtype=torch.uint8, device=dev),
+             "b": torch.empty(T, H // 16, dtype=torch.uint8, device=dev),
+             "s": torch.empty(T, dtype=torch.float32, device=dev)}
+    qkv = torch.empty(T, S.qkv_n, dtype=torch.float32, device=dev)
+    perm = {"codes": torch.empty(R, H // 2, dtype=torch.uint8, device=dev),
+            "bscales": torch.empty(R, H // 16, dtype=torch.uint8, device=dev),
+            "rscales": torch.empty(R, dtype=torch.float32, device=dev),
+            "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "row_to_tk": torch.empty(R, dtype=torch.int32, device=dev),
+            "tk_to_row": torch.empty(R, dtype=torch.int32, device=dev)}
+    gu = torch.empty(R, 2 * I, dtype=torch.float32, device=dev)
+    a2 = {"codes": torch.empty(R, I // 2, dtype=torch.uint8, device=dev),
+          "bscales": torch.empty(R, I // 16, dtype=torch.uint8, device=dev),
+          "rscales": torch.empty(R, dtype=torch.float32, device=dev)}
+    dn = torch.empty(R, H, dtype=torch.float32, device=dev)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    dy_perm = torch.empty(R, H, dtype=torch.bfloat16, device=dev)
+    dh = torch.empty(R, I, dtype=torch.float32, device=dev)
+    dgu = torch.empty(R, 2 * I, dtype=torch.bfloat16, device=dev)
+    dx_perm = torch.empty(R, H, dtype=torch.float32, device=dev)
+    dx = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    off = perm["expert_offsets"]
+    ops = [
+        ("qkv_quantize", lambda: pmg.nvfp4_quantize_rows(x, a_qkv["c"], a_qkv["b"], a_qkv["s"])),
+        ("qkv_gemm", lambda: pmg.nvfp4_grouped_gemm(a_qkv["c"], a_qkv["b"], a_qkv["s"], qkv_off, *q_qkv, c=qkv)),
+        ("quantize_permute", lambda: pmg.nvfp4_quantize_permute(x, ids, E, workspace=ws, out=perm)),
+        ("gate_up_gemm", lambda: pmg.nvfp4_grouped_gemm(perm["codes"], perm["bscales"], perm["rscales"], off,
+                                                        *q_gu, c=gu)),
+        ("swiglu_quantize", lambda: pmg.swiglu_quantize(gu, off, tw, perm["row_to_tk"], out=a2)),
+        ("down_gemm", lambda: pmg.nvfp4_grouped_gemm(a2["codes"], a2["bscales"], a2["rscales"], off, *q_d, c=dn)),
+        ("combine", lambda: pmg.unpermute_combine(dn, perm["tk_to_row"], k, y=y)),
+        ("dgrad_gather", lambda: pmg.permute_gather_bf16(dy, off, perm["row_to_tk"], k, out=dy_perm)),
+        ("dgrad_down_gemm", lambda: pmg.bf16_grouped_gemm(dy_perm, off, wd, pmg.W_KN, c=dh)),
+        ("swiglu_backward", lambda: pmg.swiglu_backward(gu, dh, off, tw, perm["row_to_tk"], dgu=dgu)),
+        ("dgrad_gate_up_gemm", lambda: pmg.bf16_grouped_gemm(dgu, off, wgu, pmg.W_KN, c=dx_perm)),
+        ("dgrad_combine", lambda: pmg.unpermute_combine(dx_perm, perm["tk_to_row"], k, y=dx)),
+    ]
+    n_ops = len(ops)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for i, (_, fn) in enumerate(ops):
+            if events is not None:
+                events[i][0].record(stream)
+            fn()
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K full steps, per-op HIP events on the launch stream
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(n_ops)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    op_ms = {name: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]))
+             for i, (name, _) in enumerate(ops)}
+
+    # ---------------- algorithmic work per op (useful rows only)
+    Rr = int(off[-1].item())
+    gemm_flops = {
+        "qkv_gemm": 2.0 * T * H * S.qkv_n,
+        "gate_up_gemm": 2.0 * Rr * H * 2 * I,
+        "down_gemm": 2.0 * Rr * I * H,
+        "dgrad_down_gemm": 2.0 * Rr * H * I,
+        "dgrad_gate_up_gemm": 2.0 * Rr * 2 * I * H,
+    }
+    nvfp4_row = lambda K: K // 2 + K // 16 + 4
+    op_bytes = {
+        "qkv_quantize": T * H * 2 + T * nvfp4_row(H),
+        "quantize_permute": T * H * 2 + T * k * 4 + Rr * nvfp4_row(H) + 2 * Rr * 4 + (E + 1) * 4,
+        "swiglu_quantize": Rr * 2 * I * 4 + Rr * 4 * 2 + Rr * nvfp4_row(I),
+        "combine": Rr * H * 4 + T * k * 4 + T * H * 2,
+        "dgrad_gather": T * H * 2 + Rr * 4 + Rr * H * 2,
+        "swiglu_backward": Rr * 2 * I * 4 + Rr * I * 4 + Rr * 8 + Rr * 2 * I * 2,
+        "dgrad_combine": Rr * H * 4 + T * k * 4 + T * H * 2,
+    }
+    per_op = {}
+    for name in op_ms:
+        us = op_ms[name] * 1e3
+        d = {"us": round(us, 2)}
+        if name in gemm_flops:
+            tf = gemm_flops[name] / (us * 1e-6) / 1e12
+            d.update(TFLOPs=round(tf, 1), frac_f16_mfma_peak=round(tf / PEAK_F16_TFLOPS, 4))
+        if name in op_bytes:
+            gbs = op_bytes[name] / (us * 1e-6) / 1e9
+            d.update(GBps=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBPS, 4))
+        per_op[name] = d
+
+    w4_us = (op_ms["gate_up_gemm"] + op_ms["down_gemm"]) * 1e3
+    value = (gemm_flops["gate_up_gemm"] + gemm_flops["down_gemm"]) / (w4_us * 1e-6) / 1e12
+    gu_us = op_ms["gate_up_gemm"] * 1e3
+    gu_tf = gemm_flops["gate_up_gemm"] / (gu_us * 1e-6) / 1e12
+    roofline = {"kernel": "nvfp4 grouped GEMM gate_up (grouped_gemm_kernel)", "bound": "mfma",
+                "achieved": round(gu_tf, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(gu_tf / PEAK_F16_TFLOPS, 4), "traffic": None,
+                "work_per_launch": f"{gemm_flops['gate_up_gemm']:.4e} FLOP (2 * {Rr} rows * 2048 * 1536)",
+                "avg_launch_us": round(gu_us, 2)}
+
+    result = {
+        "metric": "W4A4 grouped-GEMM TFLOP/s + quantize-permute GB/s, 30B-A3B MoE layer @4096 tok",
+        "value": round(value, 2), "unit": "TFLOP/s",
+        "quantize_permute_GBps": per_op["quantize_permute"]["GBps"],
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16 (NVFP4 operands decoded exactly; f32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-30B-A3B-shaped MoE layer: NVFP4 W4A4 forward + BF16 dgrad + dense W4A4 QKV",
+                   "tokens": T, "hidden": H, "experts": E, "topk": k, "intermediate": I,
+                   "qkv_n": S.qkv_n, "routing": args.routing, "routed_rows": Rr,
+                   "parallelism": "single GPU"},
+        "layer_tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "per_op": per_op,
+        "roofline": roofline,
+        "setup_s": round(setup_s, 1),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(x_bits, ids_np, wgu_bits, S, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(x_bits, ids, wgu_bits, S, budget_s):
+    """The oracle (as it is) on a bounded sample of the same workload, on the host cores.
+
+    Sample: the oracle's quantize-permute of all 4096 tokens, then its gate_up
+    grouped GEMM (exact dequantisation, FP64 BLAS on all cores) for the routed
+    rows of experts 0, 1, ... until the time budget is used.  The oracle's
+    weight quantisation is preparation and is not timed (as on the GPU).
+    """
+    from oracle import gemm as og, layer as ol, quantize as oq
+    threads = len(os.sched_getaffinity(0))
+    t = time.time()
+    (off, r2t, t2r), a = ol.quantize_permute_ref(x_bits, ids, S.E)
+    qp_s = time.time() - t
+    Rr = int(off[-1])
+    qp_bytes = S.T * S.H * 2 + S.T * S.k * 4 + Rr * (S.H // 2 + S.H // 16 + 4 + 8)
+    flops, g_s, e = 0.0, 0.0, 0
+    while e < S.E and g_s < budget_s:
+        w = oq.quantize_rows_bf16(wgu_bits[e])
+        rows = np.arange(off[e], off[e + 1])
+        t = time.time()
+        if rows.size:
+            og.grouped_gemm_ref(a[0][rows], a[1][rows], a[2][rows], np.array([0, rows.size]),
+                                *(v[None] for v in w))
+            flops += 2.0 * rows.size * S.H * 2 * S.I
+        g_s += time.time() - t
+        e += 1
+    return {"value": round(flops / g_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle gate_up grouped GEMM over the routed rows of experts 0..{e - 1} "
+                      f"({int(off[e] - off[0])} of {Rr} rows); oracle quantize-permute of all {S.T} tokens",
+            "quantize_permute_GBps": round(qp_bytes / qp_s / 1e9, 4),
+            "cpu": platform.processor() or platform.machine(), "seconds": round(g_s + qp_s, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+/*
+ * nvfp4moe.h - C ABI of the MI355X (gfx950) NVFP4 W4A4 MoE hot-path library.
+ *
+ * The operations are the kernels the miniTE pages describe for native NVFP4
+ * (W4A4) training of Qwen3-30B-A3B:
+ *   - "miniTE NVFP4" blog (yuxiaoba.github.io), section "Two complementary
+ *     interventions": contiguous buffers with device-side metadata instead of
+ *     per-expert splitting and repacking; amax computed during permutation or
+ *     during the weighted SwiGLU so no extra scan is needed; scale-layout
+ *     conversion fused with quantisation; forward and backward precision are
+ *     independent choices.  Same page, "Follow the numerical execution path":
+ *     per-token scaling, and identities of tokens and experts kept so results
+ *     can be compared after alignment.
+ *   - "miniTE accélère le RL en NVFP4 sur B300" (news.hamidun.com), section
+ *     "Diagnostic, alignement et noyaux rapides": optimised NVFP4 kernels,
+ *     scaling scheme and grouped GEMMs for MoE.
+ *
+ * NVFP4 storage used throughout (row-major, one row = one token or one
+ * weight output row, K = row length, K % 16 == 0):
+ *   codes   uint8 [rows][K/2]   E2M1 codes, element 2i in the low nibble of byte i
+ *   bscales uint8 [rows][K/16]  E4M3fn scale of each block of 16 elements
+ *   rscales float [rows]        FP32 second-level scale of the row
+ *   value(r, i) = e2m1(code) * e4m3(bscale[r][i/16]) * rscale[r]
+ * Quantisation of a row:  s = amax / 2688 (FP32 division; 2688 = 6 * 448);
+ * b_j = E4M3(blockamax_j / (6 * s)) (nearest-even, saturating at 448; 0 if
+ * s == 0); d_j = b_j * s; code_i = E2M1(x_i / d_j) (nearest, ties to the even
+ * grid index, saturating at 6, sign kept; a signed zero if d_j == 0).  All
+ * steps are IEEE FP32 operations without fused multiply-add, so results are
+ * bit-reproducible.
+ *
+ * Conventions for every entry point:
+ *   - All pointers are DEVICE pointers owned by the caller (the library never
+ *     allocates or frees), except where a parameter says otherwise.  Tensors
+ *     must be contiguous in the stated layout.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; nothing waits on the device and nothing reads device memory
+ *     on the host.
+ *   - Arguments are checked on the host before anything is enqueued; a check
+ *     failure returns a non-zero nvfp4_status and enqueues nothing.
+ *   - Routed rows: a routing of T tokens to k of E experts gives R = T*k
+ *     routed rows, grouped by expert; expert_offsets[E+1] (device, int32)
+ *     holds the first row of each expert and the total number of routed rows
+ *     in expert_offsets[E].  Buffers sized for R_cap = T*k rows are always
+ *     enough; rows at or beyond expert_offsets[E] are neither read nor written.
+ *   - dev_err (optional device int32, may be NULL): bit 0 is OR-ed in on the
+ *     device when a routing entry names an expert outside [0, E).  Such an
+ *     entry takes no row (tk_to_row = -1) and is skipped by every later step.
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4MOE_API __attribute__((visibility("default")))
+#define NVFP4MOE_ABI_VERSION 1
+#define NVFP4MOE_MAX_K 8192      /* longest quantised row */
+#define NVFP4MOE_MAX_EXPERTS 1024
+#define NVFP4MOE_MAX_TOPK 32
+
+typedef enum nvfp4_status {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,      /* a required pointer is NULL */
+  NVFP4_ERR_SHAPE = 2,     /* a size is out of range (K % 16 != 0, k > E, <= 0, too large) */
+  NVFP4_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
+  NVFP4_ERR_WORKSPACE = 4, /* workspace smaller than required */
+  NVFP4_ERR_LAUNCH = 5,    /* the HIP runtime reported an error when enqueuing */
+  NVFP4_ERR_ARG = 6        /* an enumerated argument has an unknown value */
+} nvfp4_status;
+
+#define NVFP4_DEVERR_BAD_EXPERT 1
+
+/* Text for a status code (static storage, never NULL). */
+NVFP4MOE_API const char* nvfp4moe_status_string(int status);
+
+/* NVFP4MOE_ABI_VERSION of the built library. */
+NVFP4MOE_API int nvfp4moe_abi_version(void);
+
+/* Bytes of device workspace nvfp4_quantize_permute needs for T tokens, top-k, E experts. */
+NVFP4MOE_API size_t nvfp4moe_permute_workspace_size(int64_t T, int32_t k, int32_t E);
+
+/*
+ * nvfp4_quantize_rows - NVFP4-quantise `rows` bf16 rows of length K, each with
+ * its own FP32 scale (per-token scaling; per output row for weights).
+ *   x        bf16 bits [rows][K]
+ *   codes    out [rows][K/2]; bscales out [rows][K/16]; rscales out [rows]
+ * Requires 1 <= K <= NVFP4MOE_MAX_K, K % 16 == 0, rows >= 0, x 16-byte aligned.
+ */
+NVFP4MOE_API int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t K,
+                                     uint8_t* codes, uint8_t* bscales, float* rscales,
+                                     void* stream);
+
+/*
+ * nvfp4_quantize_permute - route, permute and quantise MoE activations in one
+ * pass over x (the token amax is taken while the token is read for the
+ * permutation).
+ *   x          bf16 bits [T][H]
+ *   topk_ids   int32 [T][k], expert of each (token, slot)
+ * Outputs (all device, caller-allocated):
+ *   expert_offsets int32 [E+1]: first row of each expert, [E] = routed rows
+ *   tk_to_row      int32 [T*k]: row of (t, slot) at index t*k+slot, or -1
+ *   row_to_tk      int32 [T*k]: t*k+slot of each routed row (rows < offsets[E])
+ *   codes [T*k][H/2], bscales [T*k][H/16], rscales [T*k]: the NVFP4 rows of the
+ *     expert-grouped buffer; row(t, slot) holds token t's quantisation (the
+ *     same bytes for all k slots of a token).
+ * Row order: rows are grouped by expert id; inside an expert they follow
+ * (token, slot) order (a stable counting sort of the routing list).
+ * Workspace: `workspace` must hold nvfp4moe_permute_workspace_size(T, k, E)
+ * bytes (device memory; contents need not be initialised).
+ * Requires 1 <= k <= min(E, NVFP4MOE_MAX_TOPK), 1 <= E <= NVFP4MOE_MAX_EXPERTS,
+ * H % 16 == 0, H <= NVFP4MOE_MAX_K.  k = 1, E = 1 with ids all 0 is a plain
+ * per-token quantisation (dense projections).
+ */
+NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
+                                        const int32_t* topk_ids, int32_t k, int32_t E,
+                                        uint8_t* codes, uint8_t* bscales, float* rscales,
+                                        int32_t* expert_offsets, int32_t* row_to_tk,
+                                        int32_t* tk_to_row, void* workspace,
+                                        size_t workspace_bytes, int32_t* dev_err,
+                                        void* stream);
+
+/*
+ * nvfp4_grouped_gemm - grouped W4A4 expert GEMM on the expert-grouped buffer:
+ * for every expert e and row r in [offsets[e], offsets[e+1]):
+ *     c[r][n] = sum_k value_A(r, k) * value_W(e, n, k)        (C = A W_e^T)
+ * Elements are decoded exactly (e2m1 * e4m3 fits FP16) and multiplied on the
+ * matrix cores with FP32 accumulation; the two FP32 row scales are applied in
+ * the epilogue.  Error per element is within 2e-5 * sum_k |a_k w_k|.
+ *   A (activations): a_codes [R_cap][K/2], a_bscales [R_cap][K/16], a_rscales [R_cap]
+ *   W (weights):     w_codes [E][N][K/2], w_bscales [E][N][K/16], w_rscales [E][N]
+ *   c                float [R_cap][N]; only rows < expert_offsets[E] are written
+ * E = 1 with expert_offsets = {0, M} is a dense GEMM of M rows.
+ * Requires K % 128 == 0, N % 16 == 0, N >= 16, K <= 65536, all pointers
+ * 16-byte aligned.
+ */
+NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_bscales,
+                                    const float* a_rscales, const int32_t* expert_offsets,
+                                    int32_t E, int64_t R_cap, const uint8_t* w_codes,
+                                    const uint8_t* w_bscales, const float* w_rscales,
+                                    int64_t N, int64_t K, float* c, void* stream);
+
+/*
+ * swiglu_quantize - weighted SwiGLU of the gate_up output with the amax taken
+ * on the fly, then NVFP4 quantisation of each routed row (for the down GEMM).
+ *   gu        float [R_cap][2I]: gate = columns [0, I), up = columns [I, 2I)
+ *   topk_w    float [T*k] router weight of (t, slot) (NULL: weight 1)
+ *   row_to_tk int32 [R_cap] from nvfp4_quantize_permute (needed if topk_w)
+ *   h = float32( ((g / (1 + exp(-g))) * u) * w ), evaluated in FP64
+ *   codes [R_cap][I/2], bscales [R_cap][I/16], rscales [R_cap]: NVFP4 of h
+ *   h_out     float [R_cap][I] (NULL: not written)
+ * Requires I % 16 == 0, 16 <= I <= NVFP4MOE_MAX_K.
+ */
+NVFP4MOE_API int swiglu_quantize(const float* gu, int64_t R_cap, int64_t I,
+                                 const int32_t* expert_offsets, int32_t E,
+                                 const float* topk_w, const int32_t* row_to_tk,
+                                 uint8_t* codes, uint8_t* bscales, float* rscales,
+                                 float* h_out, void* stream);
+
+/*
+ * unpermute_combine - sum each token's k routed rows back into token order:
+ *   acc = w_0 * d[row(t,0)];  acc = acc + w_s * d[row(t,s)]  (s = 1..k-1)
+ * in FP32, slot order, no fused multiply-add; y[t] = bf16(acc) (nearest even).
+ * w_s = 1 when topk_w is NULL (the router weight already applied in
+ * swiglu_quantize).  Pairs with tk_to_row = -1 are skipped.
+ *   d float [R_cap][H]; tk_to_row int32 [T*k]; y bf16 bits [T][H]
+ * Requires H % 8 == 0, 1 <= k <= NVFP4MOE_MAX_TOPK.
+ */
+NVFP4MOE_API int unpermute_combine(const float* d, int64_t T, int32_t k, int64_t H,
+                                   const int32_t* tk_to_row, const float* topk_w,
+                                   uint16_t* y, void* stream);
+
+/*
+ * permute_gather_bf16 - copy token rows to their routed rows (backward input):
+ *   out[r] = x[row_to_tk[r] / k]  for r < expert_offsets[E]
+ *   x bf16 bits [T][H]; out bf16 bits [R_cap][H].  Requires H % 8 == 0.
+ */
+NVFP4MOE_API int permute_gather_bf16(const uint16_t* x, int64_t T, int64_t H, int32_t k,
+                                     const int32_t* expert_offsets, int32_t E,
+                                     const int32_t* row_to_tk, uint16_t* out, void* stream);
+
+/*
+ * bf16_grouped_gemm - BF16 grouped GEMM for the backward (dgrad):
+ *   c[r][n] = sum_k a[r][k] * W_e[k][n]   for r in expert e's rows
+ * with BF16 operands, FP32 accumulation, FP32 output.
+ *   a  bf16 bits [R_cap][K]
+ *   w  bf16 bits, layout by w_layout:
+ *        NVFP4MOE_W_KN (0): [E][K][N]  (e.g. the forward weight [E][out][in]
+ *                           used for the input gradient, contracting over out)
+ *        NVFP4MOE_W_NK (1): [E][N][K]
+ *   c  float [R_cap][N]
+ * Requires K % 32 == 0, N % 64 == 0 (NVFP4MOE_W_KN) or N % 16 == 0 (NVFP4MOE_W_NK).
+ */
+#define NVFP4MOE_W_KN 0
+#define NVFP4MOE_W_NK 1
+NVFP4MOE_API int bf16_grouped_gemm(const uint16_t* a, const int32_t* expert_offsets,
+                                   int32_t E, int64_t R_cap, const uint16_t* w,
+                                   int32_t w_layout, int64_t N, int64_t K, float* c,
+                                   void* stream);
+
+/*
+ * swiglu_backward - gradient of h = w * silu(g) * u with respect to g and u:
+ *   t = dh * w;  du = t * silu(g);  dg = (t * u) * (sig * (1 + g * (1 - sig)))
+ * with sig = 1 / (1 + exp(-g)), silu(g) = g / (1 + exp(-g)), in FP64; each
+ * result rounded once to bf16 (nearest even).
+ *   gu float [R_cap][2I] (forward gate_up output); dh float [R_cap][I]
+ *   topk_w / row_to_tk as in swiglu_quantize (NULL topk_w: w = 1)
+ *   dgu bf16 bits [R_cap][2I]: [0, I) = dg, [I, 2I) = du
+ * Requires I % 8 == 0.
+ */
+NVFP4MOE_API int swiglu_backward(const float* gu, const float* dh, int64_t R_cap, int64_t I,
+                                 const int32_t* expert_offsets, int32_t E,
+                                 const float* topk_w, const int32_t* row_to_tk,
+                                 uint16_t* dgu, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4MOE_H */

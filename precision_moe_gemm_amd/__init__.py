@@ -1,0 +1,277 @@
+"""MI355X (gfx950) NVFP4 W4A4 MoE hot path: a thin Python binding over libnvfp4moe.so.
+
+Every function here marshals arguments into the C ABI declared in
+``include/nvfp4moe.h`` and calls it on the current HIP stream; all arithmetic
+runs in the library's HIP kernels.  PyTorch supplies device memory and the
+stream only.  If the library has not been built, calls raise
+``LibraryNotBuilt`` - there is no fallback implementation.
+
+Tensor conventions: bf16 data may be passed as ``torch.bfloat16`` or as
+2-byte integer tensors holding the bits; NVFP4 codes and scales are
+``torch.uint8``; row scales, GEMM outputs and router weights ``torch.float32``;
+routing ids, offsets and identity maps ``torch.int32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+W_KN = 0
+W_NK = 1
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, "libnvfp4moe.so")
+
+
+_c = ctypes
+_P = _c.c_void_p
+_I64 = _c.c_int64
+_I32 = _c.c_int32
+
+# C signatures, in the order of include/nvfp4moe.h
+SIGNATURES = {
+    "nvfp4moe_status_string": ([_I32], _c.c_char_p),
+    "nvfp4moe_abi_version": ([], _c.c_int),
+    "nvfp4moe_permute_workspace_size": ([_I64, _I32, _I32], _c.c_size_t),
+    "nvfp4_quantize_rows": ([_P, _I64, _I64, _P, _P, _P, _P], _c.c_int),
+    "nvfp4_quantize_permute": ([_P, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                _c.c_size_t, _P, _P], _c.c_int),
+    "nvfp4_grouped_gemm": ([_P, _P, _P, _P, _I32, _I64, _P, _P, _P, _I64, _I64, _P, _P], _c.c_int),
+    "swiglu_quantize": ([_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P, _P], _c.c_int),
+    "unpermute_combine": ([_P, _I64, _I32, _I64, _P, _P, _P, _P], _c.c_int),
+    "permute_gather_bf16": ([_P, _I64, _I64, _I32, _P, _I32, _P, _P, _P], _c.c_int),
+    "bf16_grouped_gemm": ([_P, _P, _I32, _I64, _P, _I32, _I64, _I64, _P, _P], _c.c_int),
+    "swiglu_backward": ([_P, _P, _I64, _I64, _P, _I32, _P, _P, _P, _P], _c.c_int),
+}
+
+
+def load_library():
+    """Load libnvfp4moe.so (cached).  Raises LibraryNotBuilt if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise LibraryNotBuilt(
+            f"{path} is missing: build it with `python -m precision_moe_gemm_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().nvfp4moe_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise NVFP4Error(fn, status, status_string(status))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _req(t, name, dtypes, ndim=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8,)
+_F32 = (torch.float32,)
+_I32T = (torch.int32,)
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+# ---------------------------------------------------------------------- entry points
+def nvfp4_quantize_rows(x, codes=None, bscales=None, rscales=None):
+    """x bf16 [rows, K] -> (codes u8 [rows, K/2], bscales u8 [rows, K/16], rscales f32 [rows])."""
+    _req(x, "x", _BF16, 2)
+    rows, K = x.shape
+    codes = _empty((rows, K // 2), torch.uint8, x) if codes is None else codes
+    bscales = _empty((rows, K // 16), torch.uint8, x) if bscales is None else bscales
+    rscales = _empty((rows,), torch.float32, x) if rscales is None else rscales
+    _req(codes, "codes", _U8); _req(bscales, "bscales", _U8); _req(rscales, "rscales", _F32)
+    _check("nvfp4_quantize_rows", load_library().nvfp4_quantize_rows(
+        _ptr(x), rows, K, _ptr(codes), _ptr(bscales), _ptr(rscales), _stream()))
+    return codes, bscales, rscales
+
+
+def permute_workspace_size(T: int, k: int, E: int) -> int:
+    return int(load_library().nvfp4moe_permute_workspace_size(T, k, E))
+
+
+def nvfp4_quantize_permute(x, topk_ids, E: int, workspace=None, dev_err=None, out=None):
+    """Route + permute + quantise.  Returns dict with codes, bscales, rscales,
+    expert_offsets [E+1], row_to_tk [T*k], tk_to_row [T*k]."""
+    _req(x, "x", _BF16, 2)
+    _req(topk_ids, "topk_ids", _I32T, 2)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    if topk_ids.shape[0] != T:
+        raise ValueError("topk_ids must have one row per token")
+    R = T * k
+    o = out or {}
+    shapes = {"codes": ((R, H // 2), torch.uint8), "bscales": ((R, H // 16), torch.uint8),
+              "rscales": ((R,), torch.float32), "expert_offsets": ((E + 1,), torch.int32),
+              "row_to_tk": ((R,), torch.int32), "tk_to_row": ((R,), torch.int32)}
+    res = {n: o[n] if n in o else _empty(shp, dt, x) for n, (shp, dt) in shapes.items()}
+    ws_bytes = permute_workspace_size(T, k, E)
+    if ws_bytes == 0:
+        raise ValueError("invalid routing shape")
+    if workspace is None:
+        workspace = _empty((max(ws_bytes, 256),), torch.uint8, x)
+    for name in ("codes", "bscales"):
+        _req(res[name], name, _U8)
+    _req(res["rscales"], "rscales", _F32)
+    for name in ("expert_offsets", "row_to_tk", "tk_to_row"):
+        _req(res[name], name, _I32T)
+    _req(workspace, "workspace", _U8)
+    _req(dev_err, "dev_err", _I32T)
+    _check("nvfp4_quantize_permute", load_library().nvfp4_quantize_permute(
+        _ptr(x), T, H, _ptr(topk_ids), k, E, _ptr(res["codes"]), _ptr(res["bscales"]),
+        _ptr(res["rscales"]), _ptr(res["expert_offsets"]), _ptr(res["row_to_tk"]),
+        _ptr(res["tk_to_row"]), _ptr(workspace), workspace.numel(), _ptr(dev_err), _stream()))
+    return res
+
+
+def nvfp4_grouped_gemm(a_codes, a_bscales, a_rscales, expert_offsets, w_codes, w_bscales,
+                       w_rscales, c=None):
+    """C[r] = A[r] W_e^T over expert-grouped rows.  W tensors [E, N, ...].  Returns C f32 [R_cap, N]."""
+    for t, n, d in ((a_codes, "a_codes", _U8), (a_bscales, "a_bscales", _U8),
+                    (a_rscales, "a_rscales", _F32), (expert_offsets, "expert_offsets", _I32T),
+                    (w_codes, "w_codes", _U8), (w_bscales, "w_bscales", _U8),
+                    (w_rscales, "w_rscales", _F32)):
+        _req(t, n, d)
+    R_cap = a_codes.shape[0]
+    K = a_codes.shape[1] * 2
+    E = expert_offsets.numel() - 1
+    N = w_codes.shape[1]
+    if w_codes.shape[0] != E or w_codes.shape[2] * 2 != K:
+        raise ValueError("w_codes must be [E, N, K/2] with the activations' K")
+    c = _empty((R_cap, N), torch.float32, a_codes) if c is None else c
+    _req(c, "c", _F32)
+    _check("nvfp4_grouped_gemm", load_library().nvfp4_grouped_gemm(
+        _ptr(a_codes), _ptr(a_bscales), _ptr(a_rscales), _ptr(expert_offsets), E, R_cap,
+        _ptr(w_codes), _ptr(w_bscales), _ptr(w_rscales), N, K, _ptr(c), _stream()))
+    return c
+
+
+def swiglu_quantize(gu, expert_offsets, topk_w=None, row_to_tk=None, h_out=False, out=None):
+    """Weighted SwiGLU + NVFP4 quantise of routed rows.  Returns (codes, bscales, rscales, h or None)."""
+    _req(gu, "gu", _F32, 2)
+    _req(expert_offsets, "expert_offsets", _I32T)
+    _req(topk_w, "topk_w", _F32)
+    _req(row_to_tk, "row_to_tk", _I32T)
+    R_cap, I2 = gu.shape
+    I = I2 // 2
+    E = expert_offsets.numel() - 1
+    o = out or {}
+    codes = o["codes"] if "codes" in o else _empty((R_cap, I // 2), torch.uint8, gu)
+    bsc = o["bscales"] if "bscales" in o else _empty((R_cap, I // 16), torch.uint8, gu)
+    rsc = o["rscales"] if "rscales" in o else _empty((R_cap,), torch.float32, gu)
+    h = (o["h"] if "h" in o else _empty((R_cap, I), torch.float32, gu)) if h_out else None
+    _req(codes, "codes", _U8); _req(bsc, "bscales", _U8); _req(rsc, "rscales", _F32); _req(h, "h", _F32)
+    _check("swiglu_quantize", load_library().swiglu_quantize(
+        _ptr(gu), R_cap, I, _ptr(expert_offsets), E, _ptr(topk_w), _ptr(row_to_tk),
+        _ptr(codes), _ptr(bsc), _ptr(rsc), _ptr(h), _stream()))
+    return codes, bsc, rsc, h
+
+
+def unpermute_combine(d, tk_to_row, k: int, topk_w=None, y=None):
+    """y[t] = bf16(sum over slots of w * d[row(t, slot)]).  Returns y as torch.bfloat16 [T, H]."""
+    _req(d, "d", _F32, 2)
+    _req(tk_to_row, "tk_to_row", _I32T)
+    _req(topk_w, "topk_w", _F32)
+    T = tk_to_row.numel() // k
+    H = d.shape[1]
+    y = _empty((T, H), torch.bfloat16, d) if y is None else y
+    _req(y, "y", _BF16)
+    _check("unpermute_combine", load_library().unpermute_combine(
+        _ptr(d), T, k, H, _ptr(tk_to_row), _ptr(topk_w), _ptr(y), _stream()))
+    return y
+
+
+def permute_gather_bf16(x, expert_offsets, row_to_tk, k: int, out=None):
+    _req(x, "x", _BF16, 2)
+    _req(expert_offsets, "expert_offsets", _I32T)
+    _req(row_to_tk, "row_to_tk", _I32T)
+    T, H = x.shape
+    E = expert_offsets.numel() - 1
+    out = _empty((T * k, H), torch.bfloat16, x) if out is None else out
+    _req(out, "out", _BF16)
+    _check("permute_gather_bf16", load_library().permute_gather_bf16(
+        _ptr(x), T, H, k, _ptr(expert_offsets), E, _ptr(row_to_tk), _ptr(out), _stream()))
+    return out
+
+
+def bf16_grouped_gemm(a, expert_offsets, w, w_layout: int = W_KN, c=None):
+    """c[r] = a[r] @ W_e with W [E, K, N] (W_KN) or [E, N, K] (W_NK).  Returns f32 [R_cap, N]."""
+    _req(a, "a", _BF16, 2)
+    _req(expert_offsets, "expert_offsets", _I32T)
+    _req(w, "w", _BF16, 3)
+    R_cap, K = a.shape
+    E = expert_offsets.numel() - 1
+    N = w.shape[2] if w_layout == W_KN else w.shape[1]
+    kw = w.shape[1] if w_layout == W_KN else w.shape[2]
+    if kw != K or w.shape[0] != E:
+        raise ValueError("weight shape does not match a / expert_offsets")
+    c = _empty((R_cap, N), torch.float32, a) if c is None else c
+    _req(c, "c", _F32)
+    _check("bf16_grouped_gemm", load_library().bf16_grouped_gemm(
+        _ptr(a), _ptr(expert_offsets), E, R_cap, _ptr(w), w_layout, N, K, _ptr(c), _stream()))
+    return c
+
+
+def swiglu_backward(gu, dh, expert_offsets, topk_w=None, row_to_tk=None, dgu=None):
+    _req(gu, "gu", _F32, 2)
+    _req(dh, "dh", _F32, 2)
+    _req(expert_offsets, "expert_offsets", _I32T)
+    _req(topk_w, "topk_w", _F32)
+    _req(row_to_tk, "row_to_tk", _I32T)
+    R_cap, I2 = gu.shape
+    E = expert_offsets.numel() - 1
+    dgu = _empty((R_cap, I2), torch.bfloat16, gu) if dgu is None else dgu
+    _req(dgu, "dgu", _BF16)
+    _check("swiglu_backward", load_library().swiglu_backward(
+        _ptr(gu), _ptr(dh), R_cap, I2 // 2, _ptr(expert_offsets), E, _ptr(topk_w),
+        _ptr(row_to_tk), _ptr(dgu), _stream()))
+    return dgu

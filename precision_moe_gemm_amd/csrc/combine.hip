@@ -1,0 +1,157 @@
+// Un-permutation with the top-k combine, the gather of token rows to routed
+// rows, and the SwiGLU backward, for gfx950.  All three are HBM-bound
+// streaming kernels: one 64-lane wavefront per token or routed row, 16-byte
+// loads and stores per lane, rows located through the identity maps the
+// permutation produced (blog "miniTE NVFP4", yuxiaoba.github.io, §Follow the
+// numerical execution path: token and expert identities kept for alignment;
+// §Two complementary interventions: device-side metadata, independent
+// forward/backward precision).
+#include "common.h"
+
+namespace nvfp4moe {
+
+constexpr int kRows = 4;   // wavefronts per 256-thread workgroup
+
+// y[t] = bf16( ((w0 d[r0] + w1 d[r1]) + ...) + w_{k-1} d[r_{k-1}] ), FP32, slot order.
+__global__ __launch_bounds__(256) void unpermute_combine_kernel(
+    const float* __restrict__ d, int64_t T, int k, int H, const int32_t* __restrict__ tk_to_row,
+    const float* __restrict__ topk_w, uint16_t* __restrict__ y) {
+  const int64_t t = (int64_t)blockIdx.x * kRows + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  const int my_row = lane < k ? tk_to_row[t * k + lane] : -1;
+  const float my_w = (lane < k && topk_w) ? topk_w[t * k + lane] : 1.0f;
+  // The loop is wave-uniform (every lane runs every slot) because the slot's
+  // row and weight are fetched with cross-lane shuffles.
+  for (int c0 = 0; c0 < H; c0 += kWave * 4) {
+    const int base = c0 + lane * 4;
+    const bool inside = base < H;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    bool started = false;
+    for (int s = 0; s < k; ++s) {
+      const int row = __shfl(my_row, s, kWave);
+      const float w = __shfl(my_w, s, kWave);
+      if (row < 0 || !inside) continue;
+      float4 v = *reinterpret_cast<const float4*>(d + (int64_t)row * H + base);
+      if (topk_w) { v.x = w * v.x; v.y = w * v.y; v.z = w * v.z; v.w = w * v.w; }
+      if (started) { acc.x = acc.x + v.x; acc.y = acc.y + v.y; acc.z = acc.z + v.z; acc.w = acc.w + v.w; }
+      else { acc = v; started = true; }
+    }
+    if (!inside) continue;
+    uint2 o;
+    o.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+    o.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+    *reinterpret_cast<uint2*>(y + t * (int64_t)H + base) = o;
+  }
+}
+
+// out[r] = x[row_to_tk[r] / k] for every routed row r.
+__global__ __launch_bounds__(256) void permute_gather_kernel(
+    const uint16_t* __restrict__ x, int H, int k, const int32_t* __restrict__ offsets, int E,
+    const int32_t* __restrict__ row_to_tk, uint16_t* __restrict__ out) {
+  const int64_t r = (int64_t)blockIdx.x * kRows + (threadIdx.x >> 6);
+  if (r >= offsets[E]) return;
+  const int64_t t = row_to_tk[r] / k;
+  const uint16_t* src = x + t * (int64_t)H;
+  uint16_t* dst = out + r * (int64_t)H;
+  for (int base = lane_id() * 8; base < H; base += kWave * 8)
+    *reinterpret_cast<uint4*>(dst + base) = *reinterpret_cast<const uint4*>(src + base);
+}
+
+// Gradient of h = w * silu(g) * u; FP64 arithmetic in the order of the
+// definition, each output rounded once to bf16.
+__global__ __launch_bounds__(256) void swiglu_backward_kernel(
+    const float* __restrict__ gu, const float* __restrict__ dh, int I,
+    const int32_t* __restrict__ offsets, int E, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ row_to_tk, uint16_t* __restrict__ dgu) {
+  const int64_t r = (int64_t)blockIdx.x * kRows + (threadIdx.x >> 6);
+  if (r >= offsets[E]) return;
+  const float w = topk_w ? topk_w[row_to_tk[r]] : 1.0f;
+  const float* grow = gu + r * (int64_t)(2 * I);
+  const float* drow = dh + r * (int64_t)I;
+  uint16_t* orow = dgu + r * (int64_t)(2 * I);
+  for (int base = lane_id() * 8; base < I; base += kWave * 8) {
+    float gs[8], us[8], ds[8];
+    *reinterpret_cast<float4*>(gs) = *reinterpret_cast<const float4*>(grow + base);
+    *reinterpret_cast<float4*>(gs + 4) = *reinterpret_cast<const float4*>(grow + base + 4);
+    *reinterpret_cast<float4*>(us) = *reinterpret_cast<const float4*>(grow + I + base);
+    *reinterpret_cast<float4*>(us + 4) = *reinterpret_cast<const float4*>(grow + I + base + 4);
+    *reinterpret_cast<float4*>(ds) = *reinterpret_cast<const float4*>(drow + base);
+    *reinterpret_cast<float4*>(ds + 4) = *reinterpret_cast<const float4*>(drow + base + 4);
+    uint32_t og[4], ou[4];
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      uint32_t bg[2], bu[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const double g = gs[j + q], u = us[j + q];
+        double t = ds[j + q];
+        if (topk_w) t = t * (double)w;
+        const double den = 1.0 + exp(-g);
+        const double sig = 1.0 / den;
+        const double silu = g / den;
+        const double du = t * silu;
+        const double dg = (t * u) * (sig * (1.0 + g * (1.0 - sig)));
+        bg[q] = f64_to_bf16_rne(dg);
+        bu[q] = f64_to_bf16_rne(du);
+      }
+      og[j / 2] = bg[0] | (bg[1] << 16);
+      ou[j / 2] = bu[0] | (bu[1] << 16);
+    }
+    *reinterpret_cast<uint4*>(orow + base) = make_uint4(og[0], og[1], og[2], og[3]);
+    *reinterpret_cast<uint4*>(orow + I + base) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+  }
+}
+
+}  // namespace nvfp4moe
+
+using namespace nvfp4moe;
+
+extern "C" {
+
+NVFP4MOE_API int unpermute_combine(const float* d, int64_t T, int32_t k, int64_t H,
+                                   const int32_t* tk_to_row, const float* topk_w, uint16_t* y,
+                                   void* stream) {
+  if (T < 0 || k < 1 || k > NVFP4MOE_MAX_TOPK || H <= 0 || H % 8 != 0 || H > INT32_MAX / 2)
+    return NVFP4_ERR_SHAPE;
+  if (T == 0) return NVFP4_OK;
+  if (!d || !tk_to_row || !y) return NVFP4_ERR_NULL;
+  if (!aligned16(d) || !aligned16(y)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unpermute_combine_kernel<<<(unsigned)((T + kRows - 1) / kRows), 256, 0, s>>>(
+      d, T, k, (int)H, tk_to_row, topk_w, y);
+  return launch_status();
+}
+
+NVFP4MOE_API int permute_gather_bf16(const uint16_t* x, int64_t T, int64_t H, int32_t k,
+                                     const int32_t* expert_offsets, int32_t E,
+                                     const int32_t* row_to_tk, uint16_t* out, void* stream) {
+  if (T < 0 || k < 1 || k > NVFP4MOE_MAX_TOPK || H <= 0 || H % 8 != 0 || H > INT32_MAX / 2)
+    return NVFP4_ERR_SHAPE;
+  if (E < 1 || E > NVFP4MOE_MAX_EXPERTS) return NVFP4_ERR_SHAPE;
+  if (T == 0) return NVFP4_OK;
+  if (!x || !expert_offsets || !row_to_tk || !out) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(out)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t R_cap = T * k;
+  permute_gather_kernel<<<(unsigned)((R_cap + kRows - 1) / kRows), 256, 0, s>>>(
+      x, (int)H, k, expert_offsets, E, row_to_tk, out);
+  return launch_status();
+}
+
+NVFP4MOE_API int swiglu_backward(const float* gu, const float* dh, int64_t R_cap, int64_t I,
+                                 const int32_t* expert_offsets, int32_t E, const float* topk_w,
+                                 const int32_t* row_to_tk, uint16_t* dgu, void* stream) {
+  if (R_cap < 0 || I <= 0 || I % 8 != 0 || I > INT32_MAX / 4) return NVFP4_ERR_SHAPE;
+  if (E < 1 || E > NVFP4MOE_MAX_EXPERTS) return NVFP4_ERR_SHAPE;
+  if (R_cap == 0) return NVFP4_OK;
+  if (!gu || !dh || !expert_offsets || !dgu) return NVFP4_ERR_NULL;
+  if (topk_w && !row_to_tk) return NVFP4_ERR_NULL;
+  if (!aligned16(gu) || !aligned16(dh) || !aligned16(dgu)) return NVFP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  swiglu_backward_kernel<<<(unsigned)((R_cap + kRows - 1) / kRows), 256, 0, s>>>(
+      gu, dh, (int)I, expert_offsets, E, topk_w, row_to_tk, dgu);
+  return launch_status();
+}
+
+}  // extern "C"

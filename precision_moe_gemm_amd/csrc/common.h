@@ -1,0 +1,96 @@
+// Shared device helpers of the gfx950 NVFP4 MoE library: the NVFP4 codecs in
+// FP32 register arithmetic, wavefront reductions, and host-side argument checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/nvfp4moe.h"
+
+namespace nvfp4moe {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ codecs
+// E4M3fn code of a finite v >= 0: nearest with ties to even, saturating at 448.
+// Below 2^-6 the grid is the subnormal one (steps of 2^-9); v * 512 is exact and
+// rint() rounds half to even, and the count 8 is code 0x08 (= 2^-6), so the
+// subnormal and normal codes join up.  Above, the float32 significand is
+// rounded to 3 bits (round half to even on the 20 dropped bits); a carry moves
+// into the exponent field, which is the right next binade.
+__device__ __forceinline__ uint32_t e4m3_encode_nonneg(float v) {
+  if (v >= 448.0f) return 0x7Eu;
+  if (v < 0.015625f) return (uint32_t)__builtin_rintf(v * 512.0f);
+  uint32_t u = __float_as_uint(v);
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);   // biased exp: (e - 127) + 7
+}
+
+// E4M3fn code (non-negative, finite) -> float.
+__device__ __forceinline__ float e4m3_decode_nonneg(uint32_t b) {
+  uint32_t e = b >> 3, m = b & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+}
+
+// E2M1 code of r: nearest grid value of |r| in {0,.5,1,1.5,2,3,4,6}, ties to
+// the even index, saturating at 6; bit 3 = sign bit of r.  Each comparison
+// adds one index; '>' at a midpoint whose lower neighbour has an even index,
+// '>=' where the upper neighbour is even.
+__device__ __forceinline__ uint32_t e2m1_encode(float r) {
+  float m = __builtin_fabsf(r);
+  uint32_t idx = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                 (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
+                 (uint32_t)(m > 5.0f);
+  return idx | ((__float_as_uint(r) >> 28) & 8u);
+}
+
+// Code of element x in a block with dequantisation step d = b * s.  d == 0
+// (zero row or a block scale that underflowed) gives a zero of x's sign.
+__device__ __forceinline__ uint32_t e2m1_of(float x, float d) {
+  float r = d != 0.0f ? x / d : x * 0.0f;
+  return e2m1_encode(r);
+}
+
+// ------------------------------------------------------------------ wave ops
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> bf16 bits, nearest with ties to even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// double -> bf16 bits rounded once (nearest, ties to even), finite inputs.
+// Rounds the float64 significand to 8 bits directly, then narrows exactly.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double d) {
+  double a = __builtin_fabs(d);
+  if (a == 0.0) return (uint32_t)(__double_as_longlong(d) >> 48) & 0x8000u;
+  int e;
+  (void)__builtin_frexp(a, &e);            // a = m 2^e, m in [0.5, 1)
+  if (e < -125) e = -125;                  // fixed step 2^-133 below 2^-126
+  double step = __builtin_ldexp(1.0, e - 8);
+  double r = __builtin_rint(a / step) * step;
+  float f = (float)r;                      // exact (<= 8 significant bits) or inf
+  uint32_t bits = __float_as_uint(f) >> 16;
+  return bits | (d < 0.0 ? 0x8000u : 0u);
+}
+
+// ------------------------------------------------------------------ host helpers
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+}  // namespace nvfp4moe

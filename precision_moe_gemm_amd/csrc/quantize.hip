@@ -1,0 +1,396 @@
+// NVFP4 quantisation kernels for gfx950: per-row quantisation, the MoE
+// route + permute + quantise pass, and the weighted SwiGLU + quantise pass.
+//
+// Method (miniTE pages): per-token scaling (blog "miniTE NVFP4",
+// yuxiaoba.github.io, §Follow the numerical execution path); amax taken while
+// the permutation or the weighted SwiGLU reads the row, and the scale layout
+// written by the quantiser itself, in contiguous expert-grouped buffers with
+// device-side offsets (same page, §Two complementary interventions).
+//
+// Layout of the work: one 64-lane wavefront owns one row.  Lane l holds the 8
+// elements [c*512 + 8l, c*512 + 8l + 8) of every 512-element chunk c, loaded
+// with one 16-byte load per chunk (a wavefront reads 1 KiB of bf16 contiguous
+// per load instruction).  A 16-element block is held by the lane pair (2j,
+// 2j+1), so the block amax is one xor-shuffle and the row amax a wavefront
+// reduction: the row is read from HBM exactly once.  Codes of 8 elements pack
+// into one 32-bit word per lane, so every code store of a wavefront writes 256
+// contiguous bytes; four block scales pack into one word.
+#include "common.h"
+
+namespace nvfp4moe {
+
+constexpr int kRowsPerBlock = 4;           // wavefronts (rows) per 256-thread workgroup
+constexpr int kChunk = 512;                // elements per wavefront per 16-byte-per-lane load
+constexpr int kRouteChunk = 1024;          // routing entries per route workgroup
+constexpr int kRouteThreads = 256;
+
+// ------------------------------------------------------------------ row quantiser
+template <int NCH>
+struct RowCodes {
+  uint32_t q[NCH];   // packed E2M1 codes of this lane's 8 elements, chunk c
+  uint32_t b[NCH];   // E4M3 code of this lane's block, chunk c
+  float s;           // row scale (same in every lane)
+};
+
+// x[c][j] is element c*512 + 8*lane + j of the row; lanes past the end of the
+// row hold zeros.  Follows the definition step by step with IEEE FP32 ops
+// (the library is built with -ffp-contract=off, and '/' is correctly rounded).
+template <int NCH>
+__device__ __forceinline__ void quantize_lane_row(const float (&x)[NCH][8], RowCodes<NCH>& o) {
+  float bm[NCH];
+  float am = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(x[c][j]));
+    bm[c] = fmaxf(m, __shfl_xor(m, 1, kWave));   // block of 16 = lane pair
+    am = fmaxf(am, m);
+  }
+  const float a = wave_max(am);
+  const float s = a / 2688.0f;
+  const float six_s = 6.0f * s;
+  o.s = s;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const uint32_t b = (s != 0.0f) ? e4m3_encode_nonneg(bm[c] / six_s) : 0u;
+    const float d = e4m3_decode_nonneg(b) * s;
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= e2m1_of(x[c][j], d) << (4 * j);
+    o.q[c] = w;
+    o.b[c] = b;
+  }
+}
+
+// Writes one quantised row.  K % 64 == 0: lanes 0, 8, 16, ... each store four
+// block scales as one word; otherwise even lanes store one byte each.
+template <int NCH>
+__device__ __forceinline__ void store_row(const RowCodes<NCH>& o, int K, int64_t row,
+                                         uint8_t* __restrict__ codes,
+                                         uint8_t* __restrict__ bscales,
+                                         float* __restrict__ rscales) {
+  const int lane = lane_id();
+  uint8_t* crow = codes + row * (int64_t)(K / 2);
+  uint8_t* brow = bscales + row * (int64_t)(K / 16);
+  const bool packed_scales = (K & 63) == 0;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int base = c * kChunk + lane * 8;
+    const uint32_t p = o.b[c] | (__shfl_down(o.b[c], 2, kWave) << 8) |
+                       (__shfl_down(o.b[c], 4, kWave) << 16) | (__shfl_down(o.b[c], 6, kWave) << 24);
+    if (base < K) {
+      *reinterpret_cast<uint32_t*>(crow + base / 2) = o.q[c];
+      if (packed_scales) {
+        if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(brow + base / 16) = p;
+      } else if ((lane & 1) == 0) {
+        brow[base / 16] = (uint8_t)o.b[c];
+      }
+    }
+  }
+  if (lane == 0) rscales[row] = o.s;
+}
+
+template <int NCH>
+__device__ __forceinline__ void load_bf16_row(const uint16_t* __restrict__ xrow, int K,
+                                              float (&x)[NCH][8]) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int base = c * kChunk + lane * 8;
+    if (base < K) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xrow + base);
+      x[c][0] = bf16_lo(v.x); x[c][1] = bf16_hi(v.x);
+      x[c][2] = bf16_lo(v.y); x[c][3] = bf16_hi(v.y);
+      x[c][4] = bf16_lo(v.z); x[c][5] = bf16_hi(v.z);
+      x[c][6] = bf16_lo(v.w); x[c][7] = bf16_hi(v.w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[c][j] = 0.0f;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ kernels
+template <int NCH>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int K, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ bscales, float* __restrict__ rscales) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float v[NCH][8];
+  load_bf16_row<NCH>(x + row * (int64_t)K, K, v);
+  RowCodes<NCH> o;
+  quantize_lane_row<NCH>(v, o);
+  store_row<NCH>(o, K, row, codes, bscales, rscales);
+}
+
+// One wavefront per token: read and quantise the token once, then write the
+// same bytes to each of its k routed rows.
+template <int NCH>
+__global__ __launch_bounds__(256) void quantize_scatter_kernel(
+    const uint16_t* __restrict__ x, int64_t T, int K, int k, const int32_t* __restrict__ tk_to_row,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales, float* __restrict__ rscales) {
+  const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  const int my_row = lane < k ? tk_to_row[t * k + lane] : -1;
+  float v[NCH][8];
+  load_bf16_row<NCH>(x + t * (int64_t)K, K, v);
+  RowCodes<NCH> o;
+  quantize_lane_row<NCH>(v, o);
+  for (int slot = 0; slot < k; ++slot) {
+    const int row = __shfl(my_row, slot, kWave);
+    if (row >= 0) store_row<NCH>(o, K, row, codes, bscales, rscales);
+  }
+}
+
+// Per-chunk expert histogram (counts are order-free, so LDS atomics are fine).
+__global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int32_t* __restrict__ chunk_hist,
+    int32_t* __restrict__ dev_err) {
+  __shared__ int32_t h[NVFP4MOE_MAX_EXPERTS];
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) h[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kRouteChunk;
+  bool bad = false;
+  for (int i = threadIdx.x; i < kRouteChunk; i += kRouteThreads) {
+    const int64_t idx = base + i;
+    if (idx < n) {
+      const int e = ids[idx];
+      if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+      else bad = true;
+    }
+  }
+  if (bad && dev_err) atomicOr(dev_err, NVFP4_DEVERR_BAD_EXPERT);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) chunk_hist[(int64_t)blockIdx.x * E + e] = h[e];
+}
+
+// Offsets, and the stable rank of every routing entry of this chunk: row =
+// offsets[e] + (entries of e in earlier chunks) + (earlier entries of e in
+// this chunk).  Inside the chunk, 64 entries at a time, in order: lanes with
+// the same expert find each other with one ballot per bit of the expert id.
+__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t n, int E, int nchunks,
+    const int32_t* __restrict__ chunk_hist, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_to_tk, int32_t* __restrict__ tk_to_row) {
+  __shared__ int32_t base[NVFP4MOE_MAX_EXPERTS];
+  __shared__ int32_t tot[NVFP4MOE_MAX_EXPERTS];
+  const int c = blockIdx.x;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    int t = 0, pre = 0;
+    for (int j = 0; j < nchunks; ++j) {
+      const int v = chunk_hist[(int64_t)j * E + e];
+      t += v;
+      pre += (j < c) ? v : 0;
+    }
+    tot[e] = t;
+    base[e] = pre;
+  }
+  __syncthreads();
+  if (wave == 0) {                         // exclusive scan of the totals
+    int carry = 0;
+    for (int e0 = 0; e0 < E; e0 += kWave) {
+      const int e = e0 + lane;
+      const int v = e < E ? tot[e] : 0;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += y;
+      }
+      if (e < E) {
+        base[e] += carry + incl - v;
+        if (c == 0) offsets[e] = carry + incl - v;
+      }
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (c == 0 && lane == 0) offsets[E] = carry;
+  }
+  __syncthreads();
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  for (int sub = 0; sub < kRouteChunk / kRouteThreads; ++sub) {
+    for (int w = 0; w < kRouteThreads / kWave; ++w) {
+      if (wave == w) {
+        const int64_t idx = (int64_t)c * kRouteChunk + sub * kRouteThreads + w * kWave + lane;
+        const int e = idx < n ? ids[idx] : -1;
+        const bool valid = idx < n && e >= 0 && e < E;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+          const bool bit = valid && ((e >> b) & 1);
+          const uint64_t bb = __ballot(bit);
+          peers &= bit ? bb : ~bb;
+        }
+        const int rank = __popcll(peers & lt_mask);
+        int row = -1;
+        if (valid) row = base[e] + rank;
+        if (valid && rank == 0) base[e] = row + __popcll(peers);
+        if (idx < n) tk_to_row[idx] = row;
+        if (valid) row_to_tk[row] = (int32_t)idx;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Weighted SwiGLU on one routed row, evaluated in FP64 and rounded once to
+// FP32, then the row quantiser; the amax is taken on the values just made.
+template <int NCH>
+__global__ __launch_bounds__(256) void swiglu_quantize_kernel(
+    const float* __restrict__ gu, int I, const int32_t* __restrict__ offsets, int E,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ row_to_tk,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales, float* __restrict__ rscales,
+    float* __restrict__ h_out) {
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= offsets[E]) return;
+  const int lane = lane_id();
+  const float* grow = gu + r * (int64_t)(2 * I);
+  const float w = topk_w ? topk_w[row_to_tk[r]] : 1.0f;
+  float h[NCH][8];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int base = c * kChunk + lane * 8;
+    if (base < I) {
+      const float4 g0 = *reinterpret_cast<const float4*>(grow + base);
+      const float4 g1 = *reinterpret_cast<const float4*>(grow + base + 4);
+      const float4 u0 = *reinterpret_cast<const float4*>(grow + I + base);
+      const float4 u1 = *reinterpret_cast<const float4*>(grow + I + base + 4);
+      const float gs[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      const float us[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const double g = gs[j];
+        const double e = exp(-g);
+        double hv = (g / (1.0 + e)) * (double)us[j];
+        if (topk_w) hv = hv * (double)w;
+        h[c][j] = (float)hv;
+      }
+      if (h_out) {
+        float* hrow = h_out + r * (int64_t)I + base;
+        *reinterpret_cast<float4*>(hrow) = make_float4(h[c][0], h[c][1], h[c][2], h[c][3]);
+        *reinterpret_cast<float4*>(hrow + 4) = make_float4(h[c][4], h[c][5], h[c][6], h[c][7]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[c][j] = 0.0f;
+    }
+  }
+  RowCodes<NCH> o;
+  quantize_lane_row<NCH>(h, o);
+  store_row<NCH>(o, I, r, codes, bscales, rscales);
+}
+
+// ------------------------------------------------------------------ dispatch
+inline int nch_for(int64_t K) {
+  return K <= 512 ? 1 : K <= 1024 ? 2 : K <= 2048 ? 4 : K <= 4096 ? 8 : 16;
+}
+
+#define NVFP4_DISPATCH_NCH(K, KERNEL, GRID, STREAM, ...)                                \
+  switch (nch_for(K)) {                                                                 \
+    case 1: KERNEL<1><<<GRID, 256, 0, STREAM>>>(__VA_ARGS__); break;                    \
+    case 2: KERNEL<2><<<GRID, 256, 0, STREAM>>>(__VA_ARGS__); break;                    \
+    case 4: KERNEL<4><<<GRID, 256, 0, STREAM>>>(__VA_ARGS__); break;                    \
+    case 8: KERNEL<8><<<GRID, 256, 0, STREAM>>>(__VA_ARGS__); break;                    \
+    default: KERNEL<16><<<GRID, 256, 0, STREAM>>>(__VA_ARGS__); break;                  \
+  }
+
+inline int64_t route_chunks(int64_t T, int32_t k) {
+  const int64_t n = T * (int64_t)k;
+  return n > 0 ? (n + kRouteChunk - 1) / kRouteChunk : 1;
+}
+
+}  // namespace nvfp4moe
+
+using namespace nvfp4moe;
+
+extern "C" {
+
+NVFP4MOE_API const char* nvfp4moe_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4_ERR_SHAPE: return "a size argument is out of range";
+    case NVFP4_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case NVFP4_ERR_WORKSPACE: return "workspace too small";
+    case NVFP4_ERR_LAUNCH: return "the HIP runtime reported an error when enqueuing";
+    case NVFP4_ERR_ARG: return "an enumerated argument has an unknown value";
+    default: return "unknown status";
+  }
+}
+
+NVFP4MOE_API int nvfp4moe_abi_version(void) { return NVFP4MOE_ABI_VERSION; }
+
+NVFP4MOE_API size_t nvfp4moe_permute_workspace_size(int64_t T, int32_t k, int32_t E) {
+  if (T < 0 || k <= 0 || E <= 0) return 0;
+  const size_t bytes = (size_t)route_chunks(T, k) * (size_t)E * sizeof(int32_t);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+NVFP4MOE_API int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,
+                                     uint8_t* bscales, float* rscales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 16 != 0 || K > NVFP4MOE_MAX_K) return NVFP4_ERR_SHAPE;
+  if (rows == 0) return NVFP4_OK;
+  if (!x || !codes || !bscales || !rscales) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(bscales) || !aligned16(rscales))
+    return NVFP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  NVFP4_DISPATCH_NCH(K, quantize_rows_kernel, grid, s, x, rows, (int)K, codes, bscales, rscales);
+  return launch_status();
+}
+
+NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
+                                        const int32_t* topk_ids, int32_t k, int32_t E,
+                                        uint8_t* codes, uint8_t* bscales, float* rscales,
+                                        int32_t* expert_offsets, int32_t* row_to_tk,
+                                        int32_t* tk_to_row, void* workspace,
+                                        size_t workspace_bytes, int32_t* dev_err, void* stream) {
+  if (T < 0 || H <= 0 || H % 16 != 0 || H > NVFP4MOE_MAX_K) return NVFP4_ERR_SHAPE;
+  if (E < 1 || E > NVFP4MOE_MAX_EXPERTS || k < 1 || k > E || k > NVFP4MOE_MAX_TOPK)
+    return NVFP4_ERR_SHAPE;
+  if (T * (int64_t)k > INT32_MAX) return NVFP4_ERR_SHAPE;
+  if (!expert_offsets || !workspace) return NVFP4_ERR_NULL;
+  if (T > 0 && (!x || !topk_ids || !codes || !bscales || !rscales || !row_to_tk || !tk_to_row))
+    return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(bscales) || !aligned16(rscales) ||
+      !aligned16(workspace))
+    return NVFP4_ERR_ALIGN;
+  if (workspace_bytes < nvfp4moe_permute_workspace_size(T, k, E)) return NVFP4_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n = T * (int64_t)k;
+  const int nchunks = (int)route_chunks(T, k);
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  route_hist_kernel<<<nchunks, kRouteThreads, 0, s>>>(topk_ids, n, E, hist, dev_err);
+  route_scatter_kernel<<<nchunks, kRouteThreads, 0, s>>>(topk_ids, n, E, nchunks, hist,
+                                                         expert_offsets, row_to_tk, tk_to_row);
+  if (T > 0) {
+    const dim3 grid((unsigned)((T + kRowsPerBlock - 1) / kRowsPerBlock));
+    NVFP4_DISPATCH_NCH(H, quantize_scatter_kernel, grid, s, x, T, (int)H, (int)k, tk_to_row,
+                       codes, bscales, rscales);
+  }
+  return launch_status();
+}
+
+NVFP4MOE_API int swiglu_quantize(const float* gu, int64_t R_cap, int64_t I,
+                                 const int32_t* expert_offsets, int32_t E, const float* topk_w,
+                                 const int32_t* row_to_tk, uint8_t* codes, uint8_t* bscales,
+                                 float* rscales, float* h_out, void* stream) {
+  if (R_cap < 0 || I < 16 || I % 16 != 0 || I > NVFP4MOE_MAX_K) return NVFP4_ERR_SHAPE;
+  if (E < 1 || E > NVFP4MOE_MAX_EXPERTS) return NVFP4_ERR_SHAPE;
+  if (R_cap == 0) return NVFP4_OK;
+  if (!gu || !expert_offsets || !codes || !bscales || !rscales) return NVFP4_ERR_NULL;
+  if (topk_w && !row_to_tk) return NVFP4_ERR_NULL;
+  if (!aligned16(gu) || !aligned16(codes) || !aligned16(bscales) || !aligned16(rscales) ||
+      !aligned16(h_out))
+    return NVFP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((R_cap + kRowsPerBlock - 1) / kRowsPerBlock));
+  NVFP4_DISPATCH_NCH(I, swiglu_quantize_kernel, grid, s, gu, (int)I, expert_offsets, E, topk_w,
+                     row_to_tk, codes, bscales, rscales, h_out);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+"""The C-ABI library: it loads, exports every function include/nvfp4moe.h declares,
+and rejects bad arguments on the host before anything reaches a GPU.
+
+No call here passes a device pointer, so these run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import precision_moe_gemm_amd as pmg
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nvfp4moe.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH, ERR_ARG = range(7)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"NVFP4MOE_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    names = set(declared_functions())
+    for n in ("nvfp4_quantize_permute", "nvfp4_grouped_gemm", "swiglu_quantize", "unpermute_combine",
+              "nvfp4_quantize_rows", "bf16_grouped_gemm", "permute_gather_bf16", "swiglu_backward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(pmg.SIGNATURES)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.nvfp4moe_abi_version() == 1
+    for s in range(7):
+        assert pmg.status_string(s)
+    assert "unknown" in pmg.status_string(99)
+
+
+def test_workspace_size(lib):
+    assert lib.nvfp4moe_permute_workspace_size(4096, 8, 128) >= 32 * 128 * 4
+    assert lib.nvfp4moe_permute_workspace_size(0, 8, 128) >= 128 * 4
+    assert lib.nvfp4moe_permute_workspace_size(-1, 8, 128) == 0
+
+
+FAKE = 0x100000  # a 16-byte aligned non-null value; never dereferenced (calls fail before any launch)
+
+
+def test_quantize_rows_host_checks(lib):
+    f = lib.nvfp4_quantize_rows
+    assert f(FAKE, 4, 24, FAKE, FAKE, FAKE, None) == ERR_SHAPE        # K % 16
+    assert f(FAKE, 4, 8208, FAKE, FAKE, FAKE, None) == ERR_SHAPE      # K too large
+    assert f(FAKE, -1, 32, FAKE, FAKE, FAKE, None) == ERR_SHAPE
+    assert f(None, 4, 32, FAKE, FAKE, FAKE, None) == ERR_NULL
+    assert f(FAKE + 4, 4, 32, FAKE, FAKE, FAKE, None) == ERR_ALIGN
+    assert f(None, 0, 32, None, None, None, None) == OK               # nothing to do
+
+
+def test_quantize_permute_host_checks(lib):
+    f = lib.nvfp4_quantize_permute
+    ws = lib.nvfp4moe_permute_workspace_size(64, 8, 128)
+    args = lambda **kw: [kw.get("x", FAKE), kw.get("T", 64), kw.get("H", 256), kw.get("ids", FAKE),
+                         kw.get("k", 8), kw.get("E", 128), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         kw.get("ws", FAKE), kw.get("wsb", ws), None, None]
+    assert f(*args(k=9, E=8)) == ERR_SHAPE                  # k > E
+    assert f(*args(k=0)) == ERR_SHAPE
+    assert f(*args(k=33, E=64)) == ERR_SHAPE                # k above the supported maximum
+    assert f(*args(E=2000)) == ERR_SHAPE
+    assert f(*args(H=40)) == ERR_SHAPE                      # H % 16
+    assert f(*args(ids=None)) == ERR_NULL
+    assert f(*args(ws=None)) == ERR_NULL
+    assert f(*args(wsb=ws - 1)) == ERR_WORKSPACE
+    assert f(*args(x=FAKE + 8)) == ERR_ALIGN
+
+
+def test_gemm_host_checks(lib):
+    f = lib.nvfp4_grouped_gemm
+    base = dict(E=128, R=32768, N=1536, K=2048)
+    call = lambda **kw: f(FAKE, FAKE, FAKE, FAKE, kw.get("E", 128), kw.get("R", 32768), FAKE, FAKE,
+                          kw.get("wr", FAKE), kw.get("N", 1536), kw.get("K", 2048), kw.get("c", FAKE), None)
+    assert call(K=2000) == ERR_SHAPE                        # K % 128
+    assert call(N=1537) == ERR_SHAPE
+    assert call(E=0) == ERR_SHAPE
+    assert call(c=None) == ERR_NULL
+    assert call(wr=FAKE + 4) == ERR_ALIGN
+    g = lib.bf16_grouped_gemm
+    assert g(FAKE, FAKE, 128, 32768, FAKE, 7, 768, 2048, FAKE, None) == ERR_ARG
+    assert g(FAKE, FAKE, 128, 32768, FAKE, 0, 768, 2040, FAKE, None) == ERR_SHAPE
+
+
+def test_streaming_ops_host_checks(lib):
+    assert lib.swiglu_quantize(FAKE, 100, 40, FAKE, 4, None, None, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert lib.swiglu_quantize(FAKE, 100, 64, FAKE, 4, FAKE, None, FAKE, FAKE, FAKE, None, None) == ERR_NULL
+    assert lib.unpermute_combine(FAKE, 10, 8, 2044, FAKE, None, FAKE, None) == ERR_SHAPE
+    assert lib.unpermute_combine(FAKE, 10, 8, 2048, None, None, FAKE, None) == ERR_NULL
+    assert lib.permute_gather_bf16(FAKE, 10, 2048, 8, FAKE, 0, FAKE, FAKE, None) == ERR_SHAPE
+    assert lib.swiglu_backward(FAKE, FAKE, 10, 768, FAKE, 4, None, None, FAKE + 2, None) == ERR_ALIGN
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(pmg, "_LIB", None)
+    monkeypatch.setattr(pmg, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(pmg.LibraryNotBuilt):
+        pmg.load_library()

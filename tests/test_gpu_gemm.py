@@ -1,0 +1,117 @@
+"""GPU parity: grouped NVFP4 GEMM against the exact-dequantisation FP64 oracle.
+
+Bar: |C_gpu - C_ref| <= 2e-5 * sum_k |a_k w_k| for every compared element.
+Small cases compare every element; the full 32768 x 1536 x 2048 gate_up and
+the QKV / down shapes compare all rows of a few experts plus random rows (the
+oracle computes rows one expert at a time).
+"""
+import numpy as np
+import pytest
+import torch
+
+import precision_moe_gemm_amd as pmg
+import workloads as W
+from oracle import gemm as og, layer as ol, permute as op, quantize as oq
+from helpers import (assert_within, bf16_dev, dev, host, gpu_ready, quantize_weights_gpu,
+                     quantize_weights_oracle, sample_rows)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_ready(), reason="needs a GPU")]
+
+
+def test_tiny_single_expert_gemm():
+    """A [64x256] x W [128x256]^T, single expert (C = A W^T)."""
+    print("[gemm] tiny 64x128x256", flush=True)
+    a_bits = W.gaussian_bf16((64, 256), 1.0, W.CFG_TINY, 0)
+    w_bits = W.gaussian_bf16((1, 128, 256), 1.0, W.CFG_TINY, 1)
+    a = pmg.nvfp4_quantize_rows(bf16_dev(a_bits))
+    w = quantize_weights_gpu(w_bits)
+    off = np.array([0, 64], np.int32)
+    c = pmg.nvfp4_grouped_gemm(*a, dev(off), *w)
+    torch.cuda.synchronize()
+    ref, bound = og.grouped_gemm_ref(*oq.quantize_rows_bf16(a_bits), off, *quantize_weights_oracle(w_bits))
+    print("  err/bound", assert_within(host(c), ref, bound, "tiny"))
+
+
+def _routed_case(T, H, E, k, N, kind, seed):
+    x = W.activations(T, H, config=seed)
+    ids, _ = W.make_routing(kind, T, E, k, seed)
+    w_bits = W.gaussian_bf16((E, N, H), 0.02, seed, 20)
+    res = pmg.nvfp4_quantize_permute(bf16_dev(x), dev(ids), E)
+    w = quantize_weights_gpu(w_bits)
+    c = pmg.nvfp4_grouped_gemm(res["codes"], res["bscales"], res["rscales"], res["expert_offsets"], *w)
+    torch.cuda.synchronize()
+    (off, r2t, t2r), a_ref = ol.quantize_permute_ref(x, ids, E)
+    return host(c), off, a_ref, w_bits
+
+
+@pytest.mark.parametrize("T,H,E,k,N,kind", [
+    (512, 256, 8, 4, 256, "uniform"),      # several m/n tiles per expert, ragged tails
+    (300, 512, 16, 2, 144, "zipf"),        # N not a multiple of the 128-column tile
+    (64, 128, 32, 8, 16, "uniform"),       # smallest K step and N; many tiny experts
+    (33, 384, 128, 8, 64, "zipf"),         # empty experts, 1-row experts
+])
+def test_grouped_gemm_small_all_elements(T, H, E, k, N, kind):
+    print(f"[gemm] T={T} H={H} E={E} k={k} N={N} {kind}", flush=True)
+    c, off, a_ref, w_bits = _routed_case(T, H, E, k, N, kind, seed=31)
+    ref, bound = og.grouped_gemm_ref(*a_ref, off, *quantize_weights_oracle(w_bits))
+    R = int(off[-1])
+    print("  err/bound", assert_within(c[:R], ref, bound, "small"))
+
+
+@pytest.mark.parametrize("kind", ["uniform", "zipf"])
+def test_gate_up_full_size_sampled(kind):
+    """32768 routed rows (top-8 of 4096 tokens, 128 experts), K=2048, N=1536."""
+    print(f"[gemm] gate_up full {kind}", flush=True)
+    c, off, a_ref, w_bits = _routed_case(4096, 2048, 128, 8, 1536, kind, seed=W.CFG_GATEUP)
+    counts = np.diff(off)
+    rows, experts = sample_rows(off, [int(np.argmax(counts)), int(np.argmin(counts)), 77], extra=5, seed=1)
+    ref, bound = og.grouped_gemm_ref(*a_ref, off, *quantize_weights_oracle(w_bits, experts), rows=rows)
+    print("  rows", rows.size, "err/bound", assert_within(c[rows], ref, bound, f"gate_up {kind}"))
+    assert np.isfinite(c[: int(off[-1])]).all()
+
+
+def test_down_shape_sampled():
+    """K=768, N=2048 over 128 experts (the down projection's shape)."""
+    print("[gemm] down shape", flush=True)
+    T, E, k, I, H = 1024, 128, 8, 768, 2048
+    x = W.activations(T, I, config=W.CFG_DOWN)
+    ids, _ = W.make_routing("softmax", T, E, k, W.CFG_DOWN)
+    w_bits = W.gaussian_bf16((E, H, I), 0.02, W.CFG_DOWN, 21)
+    res = pmg.nvfp4_quantize_permute(bf16_dev(x), dev(ids), E)
+    w = quantize_weights_gpu(w_bits)
+    c = host(pmg.nvfp4_grouped_gemm(res["codes"], res["bscales"], res["rscales"], res["expert_offsets"], *w))
+    (off, _, _), a_ref = ol.quantize_permute_ref(x, ids, E)
+    rows, experts = sample_rows(off, [0, 5, 127], extra=5, seed=2)
+    ref, bound = og.grouped_gemm_ref(*a_ref, off, *quantize_weights_oracle(w_bits, experts), rows=rows)
+    print("  err/bound", assert_within(c[rows], ref, bound, "down"))
+
+
+def test_dense_qkv_sampled():
+    """Dense W4A4 QKV: M=4096, K=2048, N=5120 as a one-group GEMM."""
+    print("[gemm] qkv dense", flush=True)
+    x = W.activations(4096, 2048, config=W.CFG_LAYER)
+    w_bits = W.gaussian_bf16((1, 5120, 2048), 0.02, W.CFG_LAYER, 12)
+    a = pmg.nvfp4_quantize_rows(bf16_dev(x))
+    w = quantize_weights_gpu(w_bits)
+    off = np.array([0, 4096], np.int32)
+    c = host(pmg.nvfp4_grouped_gemm(*a, dev(off), *w))
+    rows = np.unique(np.concatenate([np.arange(0, 130), np.arange(3990, 4096),
+                                     np.random.default_rng(3).integers(0, 4096, 40)]))
+    ref, bound = og.grouped_gemm_ref(*oq.quantize_rows_bf16(x), off, *quantize_weights_oracle(w_bits), rows=rows)
+    print("  err/bound", assert_within(c[rows], ref, bound, "qkv"))
+
+
+def test_rows_are_batch_invariant():
+    """A token's GEMM row does not depend on how many other rows the expert has."""
+    print("[gemm] batch invariance", flush=True)
+    T, H, N = 300, 512, 256
+    x = W.activations(T, H, config=40)
+    w_bits = W.gaussian_bf16((1, N, H), 0.02, 40, 1)
+    w = quantize_weights_gpu(w_bits)
+    a = pmg.nvfp4_quantize_rows(bf16_dev(x))
+    full = host(pmg.nvfp4_grouped_gemm(*a, dev(np.array([0, T], np.int32)), *w))
+    for t0, t1 in [(0, 1), (5, 9), (130, 300)]:
+        sub = tuple(v[t0:t1].clone() for v in a)          # fresh, aligned allocations
+        part = host(pmg.nvfp4_grouped_gemm(*sub, dev(np.array([0, t1 - t0], np.int32)), *w))
+        assert np.array_equal(part, full[t0:t1])

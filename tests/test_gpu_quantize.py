@@ -1,0 +1,139 @@
+"""GPU parity: NVFP4 row quantisation and the route + permute + quantise pass.
+
+Bit-exact against the oracle: codes, block scales, row scales, expert offsets
+and both identity maps.
+"""
+import numpy as np
+import pytest
+import torch
+
+import precision_moe_gemm_amd as pmg
+import workloads as W
+from oracle import layer as ol, permute as op, quantize as oq
+from helpers import bf16_dev, dev, host, gpu_ready
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_ready(), reason="needs a GPU")]
+
+
+def _check_rows(bits, tag):
+    print(f"[quantize_rows] {tag} shape={bits.shape}", flush=True)
+    got = pmg.nvfp4_quantize_rows(bf16_dev(bits))
+    torch.cuda.synchronize()
+    ref = oq.quantize_rows_bf16(bits)
+    for g, r, name in zip(got, ref, ("codes", "bscales", "rscales")):
+        g = host(g)
+        if name == "rscales":
+            assert np.array_equal(g.view(np.uint32), r.view(np.uint32)), f"{tag}: {name}"
+        else:
+            bad = np.argwhere(g != r)
+            assert bad.size == 0, f"{tag}: {name} differs at {bad[:5].tolist()}"
+
+
+def test_quantize_rows_tiny_config():
+    _check_rows(W.gaussian_bf16((64, 256), 1.0, W.CFG_TINY, 0), "A 64x256")
+    _check_rows(W.gaussian_bf16((128, 256), 1.0, W.CFG_TINY, 1), "W 128x256")
+
+
+@pytest.mark.parametrize("K", [16, 48, 256, 512, 528, 768, 1040, 2048, 4096, 8192])
+def test_quantize_rows_lengths(K):
+    _check_rows(W.activations(37, K, config=2, tensor=K), f"K={K}")
+
+
+def test_quantize_rows_edge_values():
+    rng = np.random.default_rng(7)
+    rows = []
+    rows.append(np.zeros(64, np.float32))                                   # zero row
+    z = np.zeros(64, np.float32); z[::3] = -0.0; rows.append(z)             # signed zeros
+    t = np.zeros(64, np.float32); t[0] = 1e-30; t[16:32] = 1.1e-35; t[32:] = -1e-38
+    rows.append(t)                                                          # subnormal / zero block scales
+    rows.append(np.full(64, 3.3e38, np.float32))                            # near bf16 max
+    rows.append(np.full(64, -1e-39, np.float32))                            # bf16 subnormals
+    r = rng.standard_normal(64).astype(np.float32); r[5] = 1e6; rows.append(r)
+    ties = (np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 8) * 1.875 * 2.0 ** -8).astype(np.float32)
+    ties[::16] = 11.25 * 2.0 ** -8
+    ties[0] = 10.5
+    rows.append(ties)                                                       # E2M1 midpoints
+    x = np.stack(rows)
+    _check_rows(W.f32_to_bf16_bits(x), "edge values")
+    worked = np.array([10.5, -10.5, 0.4375, -1.3125, 2.1875, 3.0625, 4.375, 6.125, 8.75, 0.0,
+                       -0.0, 1.75, 5.25, 0.875, 7.0, 0.5] +
+                      [t * 1.875 * 2.0 ** -8 for t in (6, 1.25, -2.5, 5, 0.25, 0.75, 3.5, 1.75, 1,
+                                                        2, 3, 4, 0.5, 1.5, -6, 0)], np.float32)
+    _check_rows(W.f32_to_bf16_bits(worked[None]), "worked example")
+
+
+def _check_permute(x_bits, ids, E, tag, dev_err_expected=0):
+    print(f"[quantize_permute] {tag} T={x_bits.shape[0]} H={x_bits.shape[1]} k={ids.shape[1]} E={E}", flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    res = pmg.nvfp4_quantize_permute(bf16_dev(x_bits), dev(ids.astype(np.int32)), E, dev_err=err)
+    torch.cuda.synchronize()
+    off, r2t, t2r, nbad = op.permute(ids, E)
+    assert int(host(err)[0]) == dev_err_expected, tag
+    assert np.array_equal(host(res["expert_offsets"]), off), tag
+    assert np.array_equal(host(res["tk_to_row"]), t2r), tag
+    R = int(off[-1])
+    assert np.array_equal(host(res["row_to_tk"])[:R], r2t), tag
+    codes, bsc, rsc = oq.quantize_rows_bf16(x_bits)
+    tok = r2t.astype(np.int64) // ids.shape[1]
+    assert np.array_equal(host(res["codes"])[:R], codes[tok]), tag
+    assert np.array_equal(host(res["bscales"])[:R], bsc[tok]), tag
+    assert np.array_equal(host(res["rscales"])[:R].view(np.uint32), rsc[tok].view(np.uint32)), tag
+    return res
+
+
+def test_quantize_permute_full_config():
+    """4096 tokens x 2048, softmax top-8 of 128 experts, 1% x20 outliers."""
+    x = W.activations(4096, 2048, config=W.CFG_QPERM)
+    ids, _ = W.make_routing("softmax", 4096, 128, 8, W.CFG_QPERM)
+    res = _check_permute(x, ids, 128, "config 4096x2048 top8/128")
+    # same bytes in all k rows of a token (per-token scaling)
+    t2r = host(res["tk_to_row"]).reshape(4096, 8)
+    c = host(res["codes"])
+    assert np.all(c[t2r[:, 0]] == c[t2r[:, 7]])
+
+
+@pytest.mark.parametrize("T,E,k,kind", [(5, 4, 2, "uniform"), (1, 1, 1, "uniform"), (1, 128, 8, "uniform"),
+                                          (1000, 128, 8, "zipf"), (777, 16, 3, "uniform"),
+                                          (2049, 64, 8, "softmax"), (300, 1, 1, "uniform"),
+                                          (128, 1024, 32, "uniform")])
+def test_quantize_permute_ragged(T, E, k, kind):
+    x = W.activations(T, 256, config=9, tensor=T)
+    ids, _ = W.make_routing(kind, T, E, k, config=9)
+    _check_permute(x, ids, E, f"{kind}")
+
+
+def test_quantize_permute_empty_experts_and_zero_tokens():
+    x = W.activations(64, 512, config=9, tensor=1)
+    ids = np.tile(np.array([[3, 0]], np.int32), (64, 1))
+    _check_permute(x, ids, 6, "empty experts")
+    res = pmg.nvfp4_quantize_permute(bf16_dev(np.zeros((0, 512), np.uint16)),
+                                     dev(np.zeros((0, 2), np.int32)), 6)
+    torch.cuda.synchronize()
+    assert host(res["expert_offsets"]).tolist() == [0] * 7
+
+
+def test_quantize_permute_invalid_ids_flagged():
+    x = W.activations(40, 256, config=9, tensor=2)
+    ids, _ = W.make_routing("uniform", 40, 8, 2, config=9)
+    ids[3, 1] = 8
+    ids[17, 0] = -5
+    _check_permute(x, ids, 8, "invalid ids", dev_err_expected=1)
+
+
+def test_quantize_permute_deterministic():
+    x = bf16_dev(W.activations(2048, 2048, config=2))
+    ids = dev(W.make_routing("zipf", 2048, 128, 8, 2)[0])
+    a = pmg.nvfp4_quantize_permute(x, ids, 128)
+    b = pmg.nvfp4_quantize_permute(x, ids, 128)
+    torch.cuda.synchronize()
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+def test_dense_projection_path_k1_e1():
+    """k = 1, E = 1 with all ids 0 is plain per-token quantisation in token order."""
+    x = W.activations(300, 2048, config=5)
+    ids = np.zeros((300, 1), np.int32)
+    res = _check_permute(x, ids, 1, "k=1 E=1")
+    assert np.array_equal(host(res["row_to_tk"]), np.arange(300))

@@ -1,0 +1,155 @@
+"""GPU parity: weighted SwiGLU + quantise, combine, gather, SwiGLU backward, BF16 grouped GEMM.
+
+SwiGLU forward/backward: the GPU evaluates the same float64 sequence as the
+oracle; its exp() may differ from numpy's in the last float64 bit, which can
+change a float32 (bf16) rounding only when the oracle's float64 value lies
+within a few float64 ulps of a rounding midpoint.  Those elements (found by
+the oracle alone) are listed; every other element must match bit for bit, and
+every row without such an element must give bit-identical NVFP4 bytes.
+Combine and gather: bit-exact.  BF16 GEMM: 2e-5 * sum |a w|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import precision_moe_gemm_amd as pmg
+import workloads as W
+from oracle import combine as oc, formats as of, gemm as og, permute as op, swiglu as osw
+from helpers import assert_within, bf16_dev, bf16_host, dev, host, gpu_ready, sample_rows
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_ready(), reason="needs a GPU")]
+
+
+def _bf16_midpoint_adjacent(x64, rel=2.0 ** -40):
+    """True where x lies within rel*|x| of a bf16 rounding midpoint (neighbours from the bit pattern)."""
+    b = of.round_to_bf16(x64).astype(np.int32)
+    mag = b & 0x7FFF
+    sign = b & 0x8000
+    q = of.bf16_to_f32(b.astype(np.uint16)).astype(np.float64)
+    up = of.bf16_to_f32((sign | np.minimum(mag + 1, 0x7F7F)).astype(np.uint16)).astype(np.float64)
+    dn = of.bf16_to_f32((sign | np.maximum(mag - 1, 0)).astype(np.uint16)).astype(np.float64)
+    dist = np.minimum(np.abs(x64 - (q + up) / 2), np.abs(x64 - (q + dn) / 2))
+    return dist <= rel * np.maximum(np.abs(x64), 1e-300)
+
+
+def _routing(T, E, k, kind, seed):
+    ids, w = W.make_routing(kind, T, E, k, seed)
+    off, r2t, t2r, _ = op.permute(ids, E)
+    return ids, w, off, r2t, t2r
+
+
+def _gu(R, I, seed, scale=2.0):
+    return (W.rng(seed, 30).standard_normal((R, 2 * I)) * scale).astype(np.float32)
+
+
+@pytest.mark.parametrize("T,E,k,I,weighted", [(4096, 128, 8, 768, True), (100, 8, 2, 768, False),
+                                               (50, 4, 2, 48, True), (64, 2, 1, 4096, True)])
+def test_swiglu_quantize(T, E, k, I, weighted):
+    print(f"[swiglu_quantize] T={T} E={E} k={k} I={I} weighted={weighted}", flush=True)
+    ids, tw, off, r2t, t2r = _routing(T, E, k, "uniform", 50)
+    R = T * k
+    gu = _gu(R, I, 51)
+    codes, bsc, rsc, h = pmg.swiglu_quantize(dev(gu), dev(off), dev(tw.reshape(-1)) if weighted else None,
+                                             dev(r2t) if weighted else None, h_out=True)
+    torch.cuda.synchronize()
+    w_rows = osw.row_weights(tw, r2t) if weighted else None
+    rc, rb, rs, rh, amb = osw.swiglu_quantize_ref(gu, w_rows)
+    gh = host(h)
+    same = gh.view(np.uint32) == rh.view(np.uint32)
+    assert np.all(same | amb), f"h differs off the midpoints at {np.argwhere(~(same | amb))[:5].tolist()}"
+    clean = ~amb.any(axis=1)
+    print(f"  midpoint-adjacent elements: {int(amb.sum())}, rows excluded: {int((~clean).sum())}")
+    assert np.array_equal(host(codes)[clean], rc[clean])
+    assert np.array_equal(host(bsc)[clean], rb[clean])
+    assert np.array_equal(host(rsc)[clean].view(np.uint32), rs[clean].view(np.uint32))
+
+
+def test_swiglu_quantize_skips_rows_past_offsets():
+    """Rows at or beyond expert_offsets[E] are not written (poisoned buffers stay poisoned)."""
+    off = np.array([0, 1, 2, 2], np.int32)                      # 2 routed rows, capacity 4
+    gu = _gu(4, 64, 52)
+    codes = torch.full((4, 32), 0xAB, dtype=torch.uint8, device="cuda:0")
+    bsc = torch.full((4, 4), 0xCD, dtype=torch.uint8, device="cuda:0")
+    rsc = torch.full((4,), -7.0, dtype=torch.float32, device="cuda:0")
+    pmg.swiglu_quantize(dev(gu), dev(off), out={"codes": codes, "bscales": bsc, "rscales": rsc})
+    torch.cuda.synchronize()
+    assert np.all(host(codes)[2:] == 0xAB) and np.all(host(bsc)[2:] == 0xCD) and np.all(host(rsc)[2:] == -7.0)
+    rc, rb, rs, _, _ = osw.swiglu_quantize_ref(gu[:2])
+    assert np.array_equal(host(codes)[:2], rc)
+
+
+@pytest.mark.parametrize("T,E,k,H,weighted,bad", [(4096, 128, 8, 2048, False, False),
+                                                   (37, 16, 4, 264, True, False),
+                                                   (20, 8, 3, 64, True, True)])
+def test_unpermute_combine(T, E, k, H, weighted, bad):
+    print(f"[combine] T={T} k={k} H={H} weighted={weighted} invalid={bad}", flush=True)
+    ids, tw, _, _, _ = _routing(T, E, k, "uniform", 60)
+    if bad:
+        ids[2, 1] = E
+        ids[5, 0] = -1
+    off, r2t, t2r, _ = op.permute(ids, E)
+    R = int(off[-1])
+    d = (W.rng(60, 31).standard_normal((T * k, H)) * 3).astype(np.float32)
+    y = pmg.unpermute_combine(dev(d), dev(t2r), k, dev(tw.reshape(-1)) if weighted else None)
+    torch.cuda.synchronize()
+    ry, _ = oc.unpermute_combine_ref(d, t2r, k, tw if weighted else None)
+    assert np.array_equal(bf16_host(y), ry)
+
+
+def test_permute_gather():
+    print("[gather]", flush=True)
+    T, E, k, H = 4096, 128, 8, 2048
+    ids, tw, off, r2t, t2r = _routing(T, E, k, "softmax", 61)
+    x = W.gaussian_bf16((T, H), 1.0, 61, 32)
+    out = pmg.permute_gather_bf16(bf16_dev(x), dev(off), dev(r2t), k)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_host(out), oc.permute_gather_ref(x, r2t, k))
+
+
+@pytest.mark.parametrize("T,E,k,I,weighted", [(4096, 128, 8, 768, True), (40, 4, 2, 24, False)])
+def test_swiglu_backward(T, E, k, I, weighted):
+    print(f"[swiglu_backward] T={T} I={I}", flush=True)
+    ids, tw, off, r2t, t2r = _routing(T, E, k, "uniform", 62)
+    R = T * k
+    gu = _gu(R, I, 62)
+    dh = (W.rng(62, 33).standard_normal((R, I)) * 0.1).astype(np.float32)
+    dgu = pmg.swiglu_backward(dev(gu), dev(dh), dev(off), dev(tw.reshape(-1)) if weighted else None,
+                              dev(r2t) if weighted else None)
+    torch.cuda.synchronize()
+    w_rows = osw.row_weights(tw, r2t) if weighted else None
+    ref_bits, d64 = osw.swiglu_backward_ref(gu, dh, w_rows)
+    got = bf16_host(dgu)
+    amb = _bf16_midpoint_adjacent(d64)
+    diff = got != ref_bits
+    assert not np.any(diff & ~amb), f"{int((diff & ~amb).sum())} bf16 values differ"
+
+
+@pytest.mark.parametrize("layout", [pmg.W_KN, pmg.W_NK])
+@pytest.mark.parametrize("T,E,k,K,N,kind", [(256, 8, 4, 256, 192, "uniform"),
+                                             (40, 16, 2, 96, 64, "zipf")])
+def test_bf16_grouped_gemm_small(layout, T, E, k, K, N, kind):
+    print(f"[bf16 gemm] layout={layout} T={T} E={E} K={K} N={N}", flush=True)
+    ids, tw, off, r2t, t2r = _routing(T, E, k, kind, 63)
+    R = T * k
+    a = W.gaussian_bf16((R, K), 1.0, 63, 34)
+    w = W.gaussian_bf16((E, K, N), 0.02, 63, 35)
+    wl = w if layout == pmg.W_KN else np.ascontiguousarray(w.transpose(0, 2, 1))
+    c = host(pmg.bf16_grouped_gemm(bf16_dev(a), dev(off), bf16_dev(wl), layout))
+    ref, bound = og.bf16_grouped_gemm_ref(of.bf16_to_f32(a), off, of.bf16_to_f32(w), trans_w=False)
+    Rv = int(off[-1])
+    print("  err/bound", assert_within(c[:Rv], ref, bound, "bf16 gemm"))
+
+
+@pytest.mark.parametrize("K,N", [(2048, 768), (1536, 2048)])
+def test_bf16_dgrad_shapes_sampled(K, N):
+    """The two dgrad GEMMs: dY_perm [32768x2048] W_d[e] [2048x768]; dGU [32768x1536] W_gu[e] [1536x2048]."""
+    print(f"[bf16 gemm] dgrad K={K} N={N}", flush=True)
+    T, E, k = 4096, 128, 8
+    ids, tw, off, r2t, t2r = _routing(T, E, k, "softmax", 64)
+    a = W.gaussian_bf16((T * k, K), 1.0, 64, 36)
+    w = W.gaussian_bf16((E, K, N), 0.02, 64, 37)
+    c = host(pmg.bf16_grouped_gemm(bf16_dev(a), dev(off), bf16_dev(w), pmg.W_KN))
+    rows, _ = sample_rows(off, [0, 64, 127], extra=5, seed=4)
+    ref, bound = og.bf16_grouped_gemm_ref(of.bf16_to_f32(a), off, of.bf16_to_f32(w), trans_w=False, rows=rows)
+    print("  err/bound", assert_within(c[rows], ref, bound, "dgrad"))
