@@ -44,6 +44,19 @@ __device__ __forceinline__ uint32_t e2m1_encode(float r) {
   return idx | ((__float_as_uint(r) >> 28) & 8u);
 }
 
+// Eight ratios -> eight E2M1 codes packed into one word (element j at bits
+// 4j..4j+3) with v_cvt_scalef32_pk_fp4_f32, scale 1.0.  The hardware
+// conversion was compared with e2m1_encode on every one of the 2^32 float32
+// bit patterns (NaNs excepted), for both signs, on gfx950: identical.
+__device__ __forceinline__ uint32_t e2m1_pack8(const float (&r)[8]) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[0], r[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[2], r[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[4], r[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[6], r[7], 1.0f, 3);
+  return w;
+}
+
 // Code of element x in a block with dequantisation step d = b * s.  d == 0
 // (zero row or a block scale that underflowed) gives a zero of x's sign.
 __device__ __forceinline__ uint32_t e2m1_of(float x, float d) {

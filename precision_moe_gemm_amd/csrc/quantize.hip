@@ -55,60 +55,103 @@ __device__ __forceinline__ void quantize_lane_row(const float (&x)[NCH][8], RowC
   for (int c = 0; c < NCH; ++c) {
     const uint32_t b = (s != 0.0f) ? e4m3_encode_nonneg(bm[c] / six_s) : 0u;
     const float d = e4m3_decode_nonneg(b) * s;
-    uint32_t w = 0;
+    float r[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) w |= e2m1_of(x[c][j], d) << (4 * j);
-    o.q[c] = w;
+    for (int j = 0; j < 8; ++j) r[j] = d != 0.0f ? x[c][j] / d : x[c][j] * 0.0f;
+    o.q[c] = e2m1_pack8(r);
     o.b[c] = b;
   }
 }
 
-// Writes one quantised row.  K % 64 == 0: lanes 0, 8, 16, ... each store four
-// block scales as one word; otherwise even lanes store one byte each.
+// Block scales leave packed four per 32-bit word.  When K % 64 == 0, lane L
+// collects the four scales 4L..4L+3 (chunk L/8, owned by lanes 8(L%8) + 0, 2,
+// 4, 6) once per row, so a row's scales are written by lanes 0..K/64-1 with
+// one store instruction (up to 256 bytes) instead of 32 bytes per chunk.
 template <int NCH>
-__device__ __forceinline__ void store_row(const RowCodes<NCH>& o, int K, int64_t row,
-                                         uint8_t* __restrict__ codes,
+__device__ __forceinline__ uint32_t gather_scale_word(const RowCodes<NCH>& o, int c0) {
+  const int lane = lane_id();
+  const int w = c0 * 8 + lane;                 // word index handled by this lane
+  const int cw = w >> 3;                       // chunk of that word
+  const int src = (w & 7) * 8;                 // first owning lane
+  uint32_t word = 0;
+#pragma unroll
+  for (int cc = 0; cc < 8 && c0 + cc < NCH; ++cc) {
+    const uint32_t b0 = __shfl(o.b[c0 + cc], src, kWave);
+    const uint32_t b1 = __shfl(o.b[c0 + cc], src + 2, kWave);
+    const uint32_t b2 = __shfl(o.b[c0 + cc], src + 4, kWave);
+    const uint32_t b3 = __shfl(o.b[c0 + cc], src + 6, kWave);
+    if (cw == c0 + cc) word = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+  }
+  return word;
+}
+
+// Writes one quantised row.  Codes: one 32-bit word per lane per chunk (a
+// wavefront store covers 256 contiguous bytes).  sw[r] are the gathered
+// scale words (rounds of 64 words), used when K % 64 == 0; otherwise even
+// lanes store one scale byte each.
+template <int NCH>
+__device__ __forceinline__ void store_row(const RowCodes<NCH>& o, const uint32_t (&sw)[(NCH + 7) / 8],
+                                         int K, int64_t row, uint8_t* __restrict__ codes,
                                          uint8_t* __restrict__ bscales,
                                          float* __restrict__ rscales) {
   const int lane = lane_id();
   uint8_t* crow = codes + row * (int64_t)(K / 2);
   uint8_t* brow = bscales + row * (int64_t)(K / 16);
-  const bool packed_scales = (K & 63) == 0;
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int base = c * kChunk + lane * 8;
-    const uint32_t p = o.b[c] | (__shfl_down(o.b[c], 2, kWave) << 8) |
-                       (__shfl_down(o.b[c], 4, kWave) << 16) | (__shfl_down(o.b[c], 6, kWave) << 24);
-    if (base < K) {
-      *reinterpret_cast<uint32_t*>(crow + base / 2) = o.q[c];
-      if (packed_scales) {
-        if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(brow + base / 16) = p;
-      } else if ((lane & 1) == 0) {
-        brow[base / 16] = (uint8_t)o.b[c];
-      }
+    if (base < K) *reinterpret_cast<uint32_t*>(crow + base / 2) = o.q[c];
+  }
+  if ((K & 63) == 0) {
+#pragma unroll
+    for (int r = 0; r < (NCH + 7) / 8; ++r) {
+      const int w = r * 64 + lane;
+      if (w * 64 < K) *reinterpret_cast<uint32_t*>(brow + 4 * w) = sw[r];
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int base = c * kChunk + lane * 8;
+      if (base < K && (lane & 1) == 0) brow[base / 16] = (uint8_t)o.b[c];
     }
   }
   if (lane == 0) rscales[row] = o.s;
 }
 
 template <int NCH>
-__device__ __forceinline__ void load_bf16_row(const uint16_t* __restrict__ xrow, int K,
-                                              float (&x)[NCH][8]) {
+__device__ __forceinline__ void pack_scales(const RowCodes<NCH>& o, uint32_t (&sw)[(NCH + 7) / 8]) {
+#pragma unroll
+  for (int r = 0; r < (NCH + 7) / 8; ++r) sw[r] = gather_scale_word<NCH>(o, r * 8);
+}
+
+template <int NCH>
+__device__ __forceinline__ void load_bf16_raw(const uint16_t* __restrict__ xrow, int K, uint4 (&raw)[NCH]) {
   const int lane = lane_id();
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int base = c * kChunk + lane * 8;
-    if (base < K) {
-      const uint4 v = *reinterpret_cast<const uint4*>(xrow + base);
-      x[c][0] = bf16_lo(v.x); x[c][1] = bf16_hi(v.x);
-      x[c][2] = bf16_lo(v.y); x[c][3] = bf16_hi(v.y);
-      x[c][4] = bf16_lo(v.z); x[c][5] = bf16_hi(v.z);
-      x[c][6] = bf16_lo(v.w); x[c][7] = bf16_hi(v.w);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[c][j] = 0.0f;
-    }
+    raw[c] = base < K ? *reinterpret_cast<const uint4*>(xrow + base) : make_uint4(0u, 0u, 0u, 0u);
   }
+}
+
+template <int NCH>
+__device__ __forceinline__ void unpack_bf16(const uint4 (&raw)[NCH], float (&x)[NCH][8]) {
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const uint4 v = raw[c];
+    x[c][0] = bf16_lo(v.x); x[c][1] = bf16_hi(v.x);
+    x[c][2] = bf16_lo(v.y); x[c][3] = bf16_hi(v.y);
+    x[c][4] = bf16_lo(v.z); x[c][5] = bf16_hi(v.z);
+    x[c][6] = bf16_lo(v.w); x[c][7] = bf16_hi(v.w);
+  }
+}
+
+template <int NCH>
+__device__ __forceinline__ void load_bf16_row(const uint16_t* __restrict__ xrow, int K,
+                                              float (&x)[NCH][8]) {
+  uint4 raw[NCH];
+  load_bf16_raw<NCH>(xrow, K, raw);
+  unpack_bf16<NCH>(raw, x);
 }
 
 // ------------------------------------------------------------------ kernels
@@ -122,26 +165,49 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
   load_bf16_row<NCH>(x + row * (int64_t)K, K, v);
   RowCodes<NCH> o;
   quantize_lane_row<NCH>(v, o);
-  store_row<NCH>(o, K, row, codes, bscales, rscales);
+  uint32_t sw[(NCH + 7) / 8];
+  pack_scales<NCH>(o, sw);
+  store_row<NCH>(o, sw, K, row, codes, bscales, rscales);
 }
 
-// One wavefront per token: read and quantise the token once, then write the
-// same bytes to each of its k routed rows.
+// Each wavefront reads and quantises kTPW tokens (t, t + W, ... for W
+// wavefronts in the grid), issuing the loads of all of them before the first
+// is processed; a token is quantised once and its bytes are written to each
+// of its k routed rows.  One token per wavefront measured fastest: the more
+// wavefronts, the more loads in flight.
+constexpr int kTPW = 1;
+
 template <int NCH>
 __global__ __launch_bounds__(256) void quantize_scatter_kernel(
     const uint16_t* __restrict__ x, int64_t T, int K, int k, const int32_t* __restrict__ tk_to_row,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales, float* __restrict__ rscales) {
-  const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (t >= T) return;
+  const int64_t wid = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  const int64_t nw = (int64_t)gridDim.x * kRowsPerBlock;
   const int lane = lane_id();
-  const int my_row = lane < k ? tk_to_row[t * k + lane] : -1;
-  float v[NCH][8];
-  load_bf16_row<NCH>(x + t * (int64_t)K, K, v);
-  RowCodes<NCH> o;
-  quantize_lane_row<NCH>(v, o);
-  for (int slot = 0; slot < k; ++slot) {
-    const int row = __shfl(my_row, slot, kWave);
-    if (row >= 0) store_row<NCH>(o, K, row, codes, bscales, rscales);
+  uint4 raw[kTPW][NCH];
+  int my_row[kTPW];
+#pragma unroll
+  for (int j = 0; j < kTPW; ++j) {
+    const int64_t t = wid + j * nw;
+    if (t < T) {
+      load_bf16_raw<NCH>(x + t * (int64_t)K, K, raw[j]);
+      my_row[j] = lane < k ? tk_to_row[t * k + lane] : -1;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kTPW; ++j) {
+    const int64_t t = wid + j * nw;
+    if (t >= T) break;
+    float v[NCH][8];
+    unpack_bf16<NCH>(raw[j], v);
+    RowCodes<NCH> o;
+    quantize_lane_row<NCH>(v, o);
+    uint32_t sw[(NCH + 7) / 8];
+    pack_scales<NCH>(o, sw);
+    for (int slot = 0; slot < k; ++slot) {
+      const int row = __shfl(my_row[j], slot, kWave);
+      if (row >= 0) store_row<NCH>(o, sw, K, row, codes, bscales, rscales);
+    }
   }
 }
 
@@ -169,28 +235,70 @@ __global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
 
 // Offsets, and the stable rank of every routing entry of this chunk: row =
 // offsets[e] + (entries of e in earlier chunks) + (earlier entries of e in
-// this chunk).  Inside the chunk, 64 entries at a time, in order: lanes with
-// the same expert find each other with one ballot per bit of the expert id.
+// this chunk).  Wavefront w ranks the chunk's entries [256w, 256w+256) in
+// order, 64 at a time: lanes with the same expert find each other with one
+// ballot per bit of the expert id, and a per-wavefront counter per expert
+// carries the count to the next 64.  The wavefronts' counts are then
+// prefix-summed per expert, which orders the whole chunk.
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
     const int32_t* __restrict__ ids, int64_t n, int E, int nchunks,
     const int32_t* __restrict__ chunk_hist, int32_t* __restrict__ offsets,
     int32_t* __restrict__ row_to_tk, int32_t* __restrict__ tk_to_row) {
+  constexpr int kW = kRouteThreads / kWave;            // 4 wavefronts
+  constexpr int kPerWave = kRouteChunk / kW;           // 256 entries each
   __shared__ int32_t base[NVFP4MOE_MAX_EXPERTS];
   __shared__ int32_t tot[NVFP4MOE_MAX_EXPERTS];
+  __shared__ int32_t wcnt[kW][NVFP4MOE_MAX_EXPERTS];
   const int c = blockIdx.x;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    // 16 independent loads in flight per batch (a plain loop would wait for
+    // each load before issuing the next)
     int t = 0, pre = 0;
-    for (int j = 0; j < nchunks; ++j) {
-      const int v = chunk_hist[(int64_t)j * E + e];
-      t += v;
-      pre += (j < c) ? v : 0;
+    for (int j0 = 0; j0 < nchunks; j0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        v[u] = (j0 + u < nchunks) ? chunk_hist[(int64_t)(j0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        t += v[u];
+        pre += (j0 + u < c) ? v[u] : 0;
+      }
     }
     tot[e] = t;
     base[e] = pre;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) wcnt[w][e] = 0;
   }
   __syncthreads();
-  if (wave == 0) {                         // exclusive scan of the totals
+  // ranks inside this wavefront's 256 entries (no barrier needed: one wavefront
+  // owns wcnt[wave][*] and executes its LDS accesses in order)
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int rank[kPerWave / kWave], ex[kPerWave / kWave];
+#pragma unroll
+  for (int sub = 0; sub < kPerWave / kWave; ++sub) {
+    const int64_t idx = (int64_t)c * kRouteChunk + wave * kPerWave + sub * kWave + lane;
+    const int e = idx < n ? ids[idx] : -1;
+    const bool valid = idx < n && e >= 0 && e < E;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t bb = __ballot(bit);
+      peers &= bit ? bb : ~bb;
+    }
+    const int r = __popcll(peers & lt_mask);
+    int before = 0;
+    if (valid) before = wcnt[wave][e];
+    if (valid && r == 0) wcnt[wave][e] = before + __popcll(peers);
+    rank[sub] = before + r;
+    ex[sub] = valid ? e : -1;
+  }
+  __syncthreads();
+  // per expert: offsets (exclusive scan of totals, wavefront 0) and the
+  // prefix of the wavefront counts
+  if (wave == 0) {
     int carry = 0;
     for (int e0 = 0; e0 < E; e0 += kWave) {
       const int e = e0 + lane;
@@ -210,29 +318,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
     if (c == 0 && lane == 0) offsets[E] = carry;
   }
   __syncthreads();
-  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int sub = 0; sub < kRouteChunk / kRouteThreads; ++sub) {
-    for (int w = 0; w < kRouteThreads / kWave; ++w) {
-      if (wave == w) {
-        const int64_t idx = (int64_t)c * kRouteChunk + sub * kRouteThreads + w * kWave + lane;
-        const int e = idx < n ? ids[idx] : -1;
-        const bool valid = idx < n && e >= 0 && e < E;
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-          const bool bit = valid && ((e >> b) & 1);
-          const uint64_t bb = __ballot(bit);
-          peers &= bit ? bb : ~bb;
-        }
-        const int rank = __popcll(peers & lt_mask);
-        int row = -1;
-        if (valid) row = base[e] + rank;
-        if (valid && rank == 0) base[e] = row + __popcll(peers);
-        if (idx < n) tk_to_row[idx] = row;
-        if (valid) row_to_tk[row] = (int32_t)idx;
-      }
-      __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    int acc = base[e];
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      const int v = wcnt[w][e];
+      wcnt[w][e] = acc;
+      acc += v;
     }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int sub = 0; sub < kPerWave / kWave; ++sub) {
+    const int64_t idx = (int64_t)c * kRouteChunk + wave * kPerWave + sub * kWave + lane;
+    if (idx >= n) continue;
+    const int e = ex[sub];
+    const int row = e >= 0 ? wcnt[wave][e] + rank[sub] : -1;
+    tk_to_row[idx] = row;
+    if (e >= 0) row_to_tk[row] = (int32_t)idx;
   }
 }
 
@@ -280,7 +383,9 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
   }
   RowCodes<NCH> o;
   quantize_lane_row<NCH>(h, o);
-  store_row<NCH>(o, I, r, codes, bscales, rscales);
+  uint32_t sw[(NCH + 7) / 8];
+  pack_scales<NCH>(o, sw);
+  store_row<NCH>(o, sw, I, r, codes, bscales, rscales);
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -367,7 +472,7 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
   route_scatter_kernel<<<nchunks, kRouteThreads, 0, s>>>(topk_ids, n, E, nchunks, hist,
                                                          expert_offsets, row_to_tk, tk_to_row);
   if (T > 0) {
-    const dim3 grid((unsigned)((T + kRowsPerBlock - 1) / kRowsPerBlock));
+    const dim3 grid((unsigned)((T + kRowsPerBlock * kTPW - 1) / (kRowsPerBlock * kTPW)));
     NVFP4_DISPATCH_NCH(H, quantize_scatter_kernel, grid, s, x, T, (int)H, (int)k, tk_to_row,
                        codes, bscales, rscales);
   }
