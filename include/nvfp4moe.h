@@ -110,7 +110,9 @@ NVFP4MOE_API int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t K,
  * Row order: rows are grouped by expert id; inside an expert they follow
  * (token, slot) order (a stable counting sort of the routing list).
  * Workspace: `workspace` must hold nvfp4moe_permute_workspace_size(T, k, E)
- * bytes (device memory; contents need not be initialised).
+ * bytes (device memory; contents need not be initialised).  Calls that share
+ * one workspace must be ordered (same stream, or synchronised): overlapping
+ * calls on one workspace race.
  * Requires 1 <= k <= min(E, NVFP4MOE_MAX_TOPK), 1 <= E <= NVFP4MOE_MAX_EXPERTS,
  * H % 16 == 0, H <= NVFP4MOE_MAX_K.  k = 1, E = 1 with ids all 0 is a plain
  * per-token quantisation (dense projections).
