@@ -14,66 +14,73 @@
 // block-scaled FP4 MFMA takes one power-of-two scale per 32 elements and
 // cannot carry an E4M3 scale per 16 elements exactly.)
 //
-// Structure.  Workgroup tile 128 x 512 (rows of one expert x output columns),
-// K-step 128, 8 wavefronts (two per SIMD, so one wavefront's decode and LDS
-// traffic hide under the other's MFMAs), each owning 128 x 64 outputs as 8 x 4
-// MFMA 16x16x32 tiles (accumulators in AGPRs).  The MFMA computes C^T tiles
-// (weights as its first operand), which leaves 4 consecutive output columns in
-// each lane for 16-byte stores.
-//   * FP4 codes (64 B per row per K-step) and E4M3 scales (8 B per row) of both
-//     operands go from global memory straight into LDS (global_load_lds,
-//     two stages, no staging registers); code rows are stored as four 16-byte
-//     chunks XOR-swizzled by row, so 16-byte reads of 8 consecutive rows fall
-//     in distinct banks.
-//   * The activation tile is shared by all 8 wavefronts, so it is decoded once
-//     per K-step, cooperatively, into an FP16 tile in LDS (256 B rows, 16-byte
+// Structure.  Two independent 256-thread workgroups share each CU (about 77
+// KiB of LDS each), so one workgroup's barriers, decode and epilogue stores
+// run while the other keeps the matrix cores busy.  Workgroup tile 128 x 256
+// (rows of one expert x output columns), K-step 64; wavefront w owns the
+// columns [64w, 64w+64) for all 128 rows as 4 x 2 MFMA 32x32x16 tiles.  The
+// MFMA computes C^T tiles (weights as its first operand), which leaves 4
+// consecutive output columns in each lane for 16-byte stores.
+//   * FP4 codes (32 B per row per K-step) and E4M3 scales (4 B per row) of
+//     both operands go from global memory straight into LDS
+//     (global_load_lds) in a 3-stage ring: the loads of K-step g+3 are issued
+//     when K-step g starts, two full K-steps before they are read.
+//   * The activation tile is shared by the 4 wavefronts, so it is decoded once
+//     per K-step, cooperatively, into an FP16 tile in LDS (128 B rows, 16-byte
 //     chunks XOR-swizzled by row); each wavefront decodes only its own weight
-//     fragments, in registers, interleaved with its MFMAs.
+//     fragments, in registers.  Both decodes of K-step g+1 are interleaved with
+//     the MFMAs of K-step g, so one barrier per K-step suffices.
 //   * Decoding is v_cvt_scalef32_pk_f16_fp4 plus one packed FP16 multiply by
 //     the block scale per element pair.
-// A lane of K-group g takes the 32 elements [32g, 32g+32) of the K-step and
-// feeds 8 of them to each of 4 MFMA K-slices; both operands use the same
+// Lane half h (lanes 32h..32h+31) of every MFMA takes the elements
+// [32h, 32h+32) of the K-step, i.e. block scales 2h and 2h+1, and feeds 8 of
+// them to each of the 4 MFMA K-slices.  Both operands use the same
 // assignment, so the sum over K is complete and its order does not depend on
-// the number of rows.
+// the number of rows (or on the tile the row lands in).
+// Rows past an expert's end are never computed on: a tile with fewer than 128
+// rows skips its empty 32-row fragments, and the epilogue's buffer stores are
+// range-checked by the hardware against the tile's valid rows.
 // The grid is persistent: each workgroup walks tiles of a contiguous range
 // owned by its XCD (workgroups go to the 8 XCDs round-robin), m-tile major,
 // so the A rows and an expert's weights are reused from that XCD's L2.
 #include "common.h"
 
-namespace nvfp4moe {
-namespace g4 {
+#include <type_traits>
 
-constexpr int BM = 128, BN = 512, BK = 128;
-constexpr int kWaves = 8;
+namespace nvfp4moe {
+namespace g5 {
+
+constexpr int BM = 128, BN = 256, BK = 64;
+constexpr int kStages = 3;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowB = BK / 2;                // 64 code bytes per row per K-step
-constexpr int kScB = BK / 16;                // 8 scale bytes per row per K-step
+constexpr int kRowB = BK / 2;                // 32 code bytes per row per K-step
+constexpr int kScB = BK / 16;                // 4 scale bytes per row per K-step
 constexpr int WN = BN / kWaves;              // 64 columns per wavefront
-constexpr int FA = BM / 16, FB = WN / 16;    // 8 x 4 MFMA tiles per wavefront
-constexpr int kA16Row = BK * 2;              // 256 B per row of the decoded activation tile
+constexpr int FA = BM / 32, FB = WN / 32;    // 4 x 2 MFMA 32x32 tiles per wavefront
+constexpr int kA16Row = BK * 2;              // 128 B per row of the decoded activation tile
+constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that the range check drops
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
 struct __align__(16) Stage {
-  uint8_t a[BM * kRowB];       // 8 KiB FP4 activation codes
-  uint8_t w[BN * kRowB];       // 32 KiB FP4 weight codes
-  uint8_t as[BM * kScB];       // 1 KiB
-  uint8_t ws[BN * kScB];       // 4 KiB
+  uint8_t a[BM * kRowB];       // 4 KiB FP4 activation codes, row-major
+  uint8_t w[BN * kRowB];       // 8 KiB FP4 weight codes, row-major
+  uint8_t as[BM * kScB];       // 512 B
+  uint8_t ws[BN * kScB];       // 1 KiB (directly after as)
 };
 
 struct __align__(16) Smem {
-  Stage st[2];
-  uint8_t a16[2][BM * kA16Row];   // 2 x 32 KiB decoded activations (FP16)
+  Stage st[kStages];
+  uint8_t a16[2][BM * kA16Row];   // 2 x 16 KiB decoded activations (FP16)
   int tile_start[NVFP4MOE_MAX_EXPERTS + 1];
 };
 
-// physical 16-byte chunk of logical chunk c in row r of an FP4 code tile
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
-// byte offset of 16-byte chunk c (0..15) of row r in the FP16 activation tile
+// byte offset of 16-byte chunk c (0..7) of row r in the FP16 activation tile
 __device__ __forceinline__ int a16_off(int r, int c) { return r * kA16Row + ((c ^ (r & 7)) << 4); }
 
 // E4M3 byte b (non-negative) -> two FP16 copies of b * 2^-8.  The 7 value bits
@@ -94,19 +101,77 @@ __device__ __forceinline__ half8 decode8(uint32_t w, uint32_t sp) {
   return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-__device__ __forceinline__ uint32_t word(const uint4& v, int s) {
-  return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
+// Workgroup barrier that orders LDS only: global memory (in particular the
+// direct-to-LDS loads still in flight) is left alone, so the barrier does not
+// wait for them; their completion is waited for explicitly with vmcnt.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
+// Direct-to-LDS loads (global_load_lds): each lane's 16 (or 4) bytes at
+// base + voff land at lds + 16 * lane (4 * lane).  Issued through inline
+// assembly so that the compiler, which cannot tell which LDS bytes such a load
+// writes, does not make every later LDS read wait for all of them; the kernel
+// waits for them itself (vmcnt) before the barrier that publishes a stage.
+// The compiler does not count these loads, so its own vmcnt waits for other
+// loads only become stricter.  M0 is written here and nowhere else in the
+// kernel (no other M0-using instruction is generated).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t voff, const uint8_t* lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(m), "v"(voff), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t voff, const uint8_t* lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(m), "v"(voff), "s"(base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  // s_waitcnt with expcnt and lgkmcnt at their maxima: vmcnt(n), n in {0, 4, 5}
+  if (n == 5) __builtin_amdgcn_s_waitcnt(0x0F75);
+  else if (n == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// One tile: rows [m0, m0 + rows) of expert e (rows <= BM), columns [n0, n0 + BN).
+struct Tile {
+  int e, m0, rows, n0;
+};
+
+__device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_start, int E,
+                                        const int32_t* __restrict__ offsets) {
+  const int tm = L / n_tiles, tn = L - tm * n_tiles;
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_start[mid] <= tm) lo = mid; else hi = mid;
+  }
+  // the values are the same in every lane: keep them in scalar registers
+  Tile t;
+  t.e = __builtin_amdgcn_readfirstlane(lo);
+  t.m0 = __builtin_amdgcn_readfirstlane(offsets[t.e] + (tm - tile_start[t.e]) * BM);
+  t.rows = __builtin_amdgcn_readfirstlane(min(BM, offsets[t.e + 1] - t.m0));
+  t.n0 = tn * BN;
+  return t;
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_bscales,
     const float* __restrict__ a_rscales, const int32_t* __restrict__ offsets, int E,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_bscales,
     const float* __restrict__ w_rscales, int N, int K, float* __restrict__ c) {
   __shared__ Smem sm;
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, h = lane >> 5;
 
   // m-tiles per expert -> exclusive prefix (device-side metadata only)
   if (wave == 0) {
@@ -128,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   __syncthreads();
 
   const int n_tiles = (N + BN - 1) / BN;
-  const int total = sm.tile_start[E] * n_tiles;
+  const int total = __builtin_amdgcn_readfirstlane(sm.tile_start[E]) * n_tiles;
   // XCD-contiguous tile ranges when the grid is a multiple of 8 workgroups
   int begin, end, step;
   if ((gridDim.x & 7) == 0) {
@@ -142,177 +207,224 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     end = total;
     step = gridDim.x;
   }
+  if (begin >= end) return;
 
-  const int kb = K / 2, ks = K / 16, nk = K / BK;
-  // cooperative activation decode: lane -> row 16*wave + lane/4, K quarter lane%4
-  const int drow = 16 * wave + (lane >> 2), dq = lane & 3;
+  const uint32_t kb = (uint32_t)K / 2, ks = (uint32_t)K / 16;
+  const int nk = K / BK;
+  const int n_scale_loads = wave < 2 ? 2 : 1;   // 6 scale-load instructions over 4 wavefronts
 
-  for (int L = begin; L < end; L += step) {
-    const int tm = L / n_tiles, tn = L - tm * n_tiles;
-    int lo = 0, hi = E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (sm.tile_start[mid] <= tm) lo = mid; else hi = mid;
-    }
-    const int e = lo;
-    const int m_end = offsets[e + 1];
-    const int m0 = offsets[e] + (tm - sm.tile_start[e]) * BM;
-    const int n0 = tn * BN;
-
-    // Sources of this lane's direct-to-LDS loads, as 32-bit byte offsets from
-    // the operand bases (the host keeps every operand under 4 GiB).  A
-    // wavefront instruction fills 1 KiB of LDS (16 rows of codes; lane l ->
-    // row l/4, physical chunk l%4), so the lane loads the logical chunk that
-    // belongs in that slot.  Wavefront w loads code rows [16w, 16w+16) of A
-    // and rows 128j + [16w, 16w+16) of W; scale dwords go one per lane.
-    uint32_t off_a, off_w[4], off_s[3];
-    {
-      const int row = 16 * wave + (lane >> 2);
-      const int chunk = (lane & 3) ^ swz(row);
-      off_a = (uint32_t)min(m0 + row, m_end - 1) * (uint32_t)kb + chunk * 16;
+  // ---------------------------------------------------------------- loads
+  // Load cursor: the next K-step to load is (ltile, lk).  Each lane's sources
+  // are 32-bit byte offsets from the operand bases (the host keeps every
+  // operand under 4 GiB).  A wavefront instruction fills 1 KiB of LDS: 32 code
+  // rows (lane l -> row l/2, 16-byte half l%2) or 64 scale dwords.
+  int lL = begin, lk = 0;
+  uint32_t off_a, off_w[2], off_s[2];
+  auto set_load_tile = [&](int L) __attribute__((always_inline)) {
+    const Tile t = tile_at(L, n_tiles, sm.tile_start, E, offsets);
+    const int m_last = t.m0 + t.rows - 1;
+    const int half = lane & 1;
+    off_a = (uint32_t)min(t.m0 + 32 * wave + (lane >> 1), m_last) * kb + half * 16;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        off_w[j] = ((uint32_t)e * N + min(n0 + 128 * j + row, N - 1)) * (uint32_t)kb + chunk * 16;
-      // scale dwords: 1280 in all (A: 256, W: 1024); dword d -> row d/2, half d%2
+    for (int u = 0; u < 2; ++u)
+      off_w[u] = ((uint32_t)t.e * N + min(t.n0 + 64 * wave + 32 * u + (lane >> 1), N - 1)) * kb +
+                 half * 16;
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int d = 512 * j + tid;
-        if (d < 256)
-          off_s[j] = (uint32_t)min(m0 + (d >> 1), m_end - 1) * (uint32_t)ks + (d & 1) * 4;
-        else
-          off_s[j] = ((uint32_t)e * N + min(n0 + ((d - 256) >> 1), N - 1)) * (uint32_t)ks + (d & 1) * 4;
-      }
+    for (int u = 0; u < 2; ++u) {
+      const int q = wave + 4 * u;        // scale instruction: 0,1 -> A rows, 2..5 -> W rows
+      if (q < 2)
+        off_s[u] = (uint32_t)min(t.m0 + 64 * q + lane, m_last) * ks;
+      else
+        off_s[u] = ((uint32_t)t.e * N + min(t.n0 + 64 * (q - 2) + lane, N - 1)) * ks;
     }
-
-#define G4_ISSUE_LOADS(kt, S)                                                                      \
-    {                                                                                              \
-      __builtin_amdgcn_global_load_lds((glb_void*)(a_codes + (kt) * kRowB + off_a),                \
-                                       (lds_void*)((S).a + wave * 1024), 16, 0, 0);                \
-      _Pragma("unroll") for (int j = 0; j < 4; ++j)                                                \
-        __builtin_amdgcn_global_load_lds((glb_void*)(w_codes + (kt) * kRowB + off_w[j]),           \
-                                         (lds_void*)((S).w + (8 * j + wave) * 1024), 16, 0, 0);    \
-      /* scale dwords 0..255 -> as, 256..1279 -> ws (as and ws are adjacent) */                   \
-      _Pragma("unroll") for (int j = 0; j < 3; ++j) {                                              \
-        const int d0 = 512 * j + 64 * wave;                                                        \
-        if (d0 < 1280) {                                                                           \
-          const uint8_t* base = d0 < 256 ? a_bscales : w_bscales;                                  \
-          __builtin_amdgcn_global_load_lds((glb_void*)(base + (kt) * kScB + off_s[j]),             \
-                                           (lds_void*)((S).as + d0 * 4), 4, 0, 0);                 \
-        }                                                                                          \
-      }                                                                                            \
+  };
+  // issues the loads of the cursor's K-step into stage S and advances the
+  // cursor; returns the number of load instructions this wavefront issued
+  auto issue_loads = [&](Stage& S) __attribute__((always_inline)) -> int {
+    if (lL >= end) return 0;
+    const uint32_t ka = (uint32_t)lk * kRowB, kss = (uint32_t)lk * kScB;
+    lds_dma16(a_codes, ka + off_a, S.a + wave * 1024);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) lds_dma16(w_codes, ka + off_w[u], S.w + (2 * wave + u) * 1024);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = wave + 4 * u;
+      if (q < 6) lds_dma4(q < 2 ? a_bscales : w_bscales, kss + off_s[u], S.as + q * 256);
     }
-
-    // decode this lane's share of the activation tile of a stage into an FP16 tile:
-    // row drow, elements [32 dq, 32 dq + 32) = logical FP4 chunk dq, block scales 2dq, 2dq+1
-#define G4_DECODE_A(S, A16)                                                                        \
-    {                                                                                              \
-      const uint4 v = *reinterpret_cast<const uint4*>((S).a + drow * kRowB + ((dq ^ swz(drow)) << 4)); \
-      const uint32_t x = *reinterpret_cast<const uint16_t*>((S).as + drow * kScB + 2 * dq);        \
-      const uint32_t s0 = scale_pair(x & 0xFF), s1 = scale_pair(x >> 8);                           \
-      const half8 h0 = decode8(v.x, s0), h1 = decode8(v.y, s0);                                    \
-      const half8 h2 = decode8(v.z, s1), h3 = decode8(v.w, s1);                                    \
-      *reinterpret_cast<half8*>((A16) + a16_off(drow, 4 * dq + 0)) = h0;                           \
-      *reinterpret_cast<half8*>((A16) + a16_off(drow, 4 * dq + 1)) = h1;                           \
-      *reinterpret_cast<half8*>((A16) + a16_off(drow, 4 * dq + 2)) = h2;                           \
-      *reinterpret_cast<half8*>((A16) + a16_off(drow, 4 * dq + 3)) = h3;                           \
+    if (++lk == nk) {
+      lk = 0;
+      lL += step;
+      if (lL < end) set_load_tile(lL);
     }
+    return 3 + n_scale_loads;
+  };
 
-    floatx4 acc[FA][FB];
+  // ---------------------------------------------------------------- decodes
+  // activation decode: thread -> row tid/2, elements [32 (tid%2), +32)
+  const int drow = tid >> 1, dhalf = tid & 1;
+  uint4 da;          // raw codes of the next K-step's activation share
+  uint32_t dsc;      // its two block scales
+  auto read_a = [&](const Stage& S) __attribute__((always_inline)) {
+    da = *reinterpret_cast<const uint4*>(S.a + drow * kRowB + dhalf * 16);
+    dsc = *reinterpret_cast<const uint16_t*>(S.as + drow * kScB + dhalf * 2);
+  };
+  auto decode_a = [&](uint8_t* A16) __attribute__((always_inline)) {
+    const uint32_t s0 = scale_pair(dsc & 0xFF), s1 = scale_pair(dsc >> 8);
+    const int c0 = 4 * dhalf;
+    *reinterpret_cast<half8*>(A16 + a16_off(drow, c0 + 0)) = decode8(da.x, s0);
+    *reinterpret_cast<half8*>(A16 + a16_off(drow, c0 + 1)) = decode8(da.y, s0);
+    *reinterpret_cast<half8*>(A16 + a16_off(drow, c0 + 2)) = decode8(da.z, s1);
+    *reinterpret_cast<half8*>(A16 + a16_off(drow, c0 + 3)) = decode8(da.w, s1);
+  };
+  // weight fragments: fragment f of this wavefront = W rows 64 wave + 32 f +
+  // (lane % 32); the lane's 32 elements [32h, 32h+32) of the K-step are 16
+  // code bytes (word s = the 8 elements of MFMA slice s) and block scales 2h,
+  // 2h+1 (slices 0-1 and 2-3)
+  uint4 rb[FB];
+  uint32_t xb[FB];
+  auto read_b = [&](const Stage& S) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < FB; ++f) {
+      const int row = WN * wave + 32 * f + l32;
+      rb[f] = *reinterpret_cast<const uint4*>(S.w + row * kRowB + h * 16);
+      xb[f] = *reinterpret_cast<const uint16_t*>(S.ws + row * kScB + h * 2);
+    }
+  };
+  auto word = [](const uint4& v, int s) __attribute__((always_inline)) {
+    return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
+  };
+
+  // ---------------------------------------------------------------- prologue
+  set_load_tile(begin);
+  issue_loads(sm.st[0]);
+  issue_loads(sm.st[1]);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
+  read_a(sm.st[0]);
+  decode_a(sm.a16[0]);
+  read_b(sm.st[0]);
+  int n_last = issue_loads(sm.st[2]);   // K-step 2 (or nothing)
+
+  half8 bv[FB];
+#pragma unroll
+  for (int f = 0; f < FB; ++f) bv[f] = decode8(rb[f].x, scale_pair(xb[f] & 0xFF));
+
+  floatx16 acc[FA][FB];
+#pragma unroll
+  for (int i = 0; i < FA; ++i)
+#pragma unroll
+    for (int j = 0; j < FB; ++j) acc[i][j] = floatx16{};
+
+  // ---------------------------------------------------------------- main loop
+  int sc = 0, ab = 0;   // stage and decoded-activation buffer of the current K-step
+
+  // One K-step of MFMAs (4 slices of 16) with the decodes of the next K-step
+  // interleaved.  A fragments are read one slice ahead.  The next K-step's
+  // stage is read and decoded even when there is none: the reads stay inside
+  // LDS and what they produce is never used.  FULL: all row fragments hold
+  // rows; otherwise fragments at or past fa_eff are skipped.
+  auto mma_step = [&](auto full_tag, int fa_eff) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    const uint8_t* A16 = sm.a16[ab];
+    uint8_t* A16n = sm.a16[ab ^ 1];
+    const Stage& Sn = sm.st[sc == kStages - 1 ? 0 : sc + 1];
+    half8 av[FA], bn[FB];
 #pragma unroll
     for (int i = 0; i < FA; ++i)
+      av[i] = *reinterpret_cast<const half8*>(A16 + a16_off(32 * i + l32, 4 * h));
 #pragma unroll
-      for (int j = 0; j < FB; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    // prologue: K-step 0 loaded and decoded, K-step 1 in flight
-    G4_ISSUE_LOADS(0, sm.st[0])
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-    __syncthreads();
-    G4_DECODE_A(sm.st[0], sm.a16[0])
-    if (nk > 1) G4_ISSUE_LOADS(1, sm.st[1])
-    __syncthreads();
-
-    // raw weight fragments of the K-step (4 slices in a 16-byte read) and scales
-    uint4 rb[FB];
-    uint32_t xb[FB];
-#define G4_READ_B(S)                                                                               \
-    _Pragma("unroll") for (int f = 0; f < FB; ++f) {                                               \
-      const int row = wave * WN + f * 16 + l16;                                                    \
-      rb[f] = *reinterpret_cast<const uint4*>((S).w + row * kRowB + ((g ^ swz(row)) << 4));        \
-      xb[f] = *reinterpret_cast<const uint16_t*>((S).ws + row * kScB + 2 * g);                     \
-    }
-    G4_READ_B(sm.st[0])
-
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint8_t* A16 = sm.a16[kt & 1];
-      // MFMA D = W_frag x A_frag^T: C^T tiles.  Activation fragments come
-      // decoded from LDS (16-byte reads); the weight fragments of slice s+1
-      // are decoded in registers while slice s runs on the matrix cores.
-      half8 bv[FB], bn[FB];
+    for (int s = 0; s < 4; ++s) {
+      if (s == 0) read_a(Sn);
+      if (s == 1) decode_a(A16n);
+      // B values of the next slice (of the next K-step after slice 3)
+      if (s < 3) {
 #pragma unroll
-      for (int j = 0; j < FB; ++j) bv[j] = decode8(rb[j].x, scale_pair(xb[j] & 0xFF));
+        for (int j = 0; j < FB; ++j)
+          bn[j] = decode8(word(rb[j], s + 1), scale_pair(s + 1 < 2 ? (xb[j] & 0xFF) : (xb[j] >> 8)));
+      }
+      if (s == 2) read_b(Sn);
+      if (s == 3) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+        for (int j = 0; j < FB; ++j) bn[j] = decode8(rb[j].x, scale_pair(xb[j] & 0xFF));
+      }
 #pragma unroll
-        for (int i = 0; i < FA; ++i) {
-          const half8 av = *reinterpret_cast<const half8*>(A16 + a16_off(i * 16 + l16, 4 * g + s));
-          if (s + 1 < 4 && i < FB)
-            bn[i] = decode8(word(rb[i], s + 1), scale_pair(s + 1 < 2 ? (xb[i] & 0xFF) : (xb[i] >> 8)));
+      for (int i = 0; i < FA; ++i) {
+        const half8 a = av[i];
+        if (s < 3) av[i] = *reinterpret_cast<const half8*>(A16 + a16_off(32 * i + l32, 4 * h + s + 1));
+        if (FULL || i < fa_eff) {
 #pragma unroll
           for (int j = 0; j < FB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv[j], av, acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], a, acc[i][j], 0, 0, 0);
         }
-        if (s + 1 < 4) {
+      }
 #pragma unroll
-          for (int j = 0; j < FB; ++j) bv[j] = bn[j];
-        }
-      }
-      if (kt + 1 < nk) {
-        const Stage& S1 = sm.st[(kt + 1) & 1];
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this lane's loads of K-step kt+1 landed
-        __syncthreads();                      // everyone's; all reads of a16[kt&1] and stage kt&1 done
-        G4_READ_B(S1)
-        G4_DECODE_A(S1, sm.a16[(kt + 1) & 1])
-        if (kt + 2 < nk) G4_ISSUE_LOADS(kt + 2, sm.st[kt & 1])
-        __syncthreads();                      // decoded activations visible
-      }
+      for (int j = 0; j < FB; ++j) bv[j] = bn[j];
     }
-#undef G4_ISSUE_LOADS
-#undef G4_DECODE_A
-#undef G4_READ_B
+  };
 
-    // epilogue: C = (acc * s_A[row]) * s_W[col].  Tile (i, j) of the lane holds
-    // row 16i + l16 and columns 16j + 4g .. 16j + 4g + 3: one 16-byte store.
-    float4 swv[FB];
-#pragma unroll
-    for (int j = 0; j < FB; ++j) {
-      const int n = n0 + wave * WN + j * 16 + 4 * g;
-      swv[j] = n < N ? *reinterpret_cast<const float4*>(w_rscales + (int64_t)e * N + n)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  // The K-steps of one tile.  At the top of each: the loads of the next
+  // K-step have landed (those of the one after may still be in flight, unless
+  // epilogue stores are pending, whose completion order against loads is not
+  // guaranteed); the barrier publishes them and the decoded activations of
+  // this K-step, and frees the stage that the new loads go to.
+  auto run_tile = [&](auto full_tag, int fa_eff, bool after_stores) __attribute__((always_inline)) {
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt(kt == 0 && after_stores ? 0 : n_last);
+      lds_barrier();
+      n_last = issue_loads(sm.st[sc]);
+      mma_step(full_tag, fa_eff);
+      sc = sc == kStages - 1 ? 0 : sc + 1;
+      ab ^= 1;
     }
+  };
+
+  for (int L = begin; L < end; L += step) {
+    const Tile t = tile_at(L, n_tiles, sm.tile_start, E, offsets);
+    const int fa_eff = (t.rows + 31) >> 5;
+    if (fa_eff == FA) run_tile(std::true_type{}, FA, L != begin);
+    else run_tile(std::false_type{}, fa_eff, L != begin);
+
+    // epilogue: C = (acc * s_A[row]) * s_W[col].  Tile (i, j) of the lane
+    // holds row 32i + lane%32 and, for q = 0..3, columns 32j + 8q + 4h .. +3:
+    // 16-byte stores.  Rows past the tile's valid rows fall outside the
+    // buffer's range and are dropped by the hardware; columns past N get an
+    // out-of-range offset.  (The row scales are read here rather than ahead:
+    // kept in registers across the K-step they would not fit.)
+    float sa[FA];
+    float4 swv[FB][4];
+#pragma unroll
+    for (int i = 0; i < FA; ++i) sa[i] = a_rscales[t.m0 + min(32 * i + l32, t.rows - 1)];
+#pragma unroll
+    for (int j = 0; j < FB; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = t.n0 + WN * wave + 32 * j + 8 * q + 4 * h;
+        swv[j][q] = *reinterpret_cast<const float4*>(w_rscales + (int64_t)t.e * N + min(n, N - 4));
+      }
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        c + (int64_t)t.m0 * N, (short)0, t.rows * N * 4, 0x00020000);
 #pragma unroll
     for (int i = 0; i < FA; ++i) {
-      const int r = m0 + i * 16 + l16;
-      if (r < m_end) {
-        const float sav = a_rscales[r];
-        float* crow = c + (int64_t)r * N + n0 + wave * WN + 4 * g;
 #pragma unroll
-        for (int j = 0; j < FB; ++j) {
-          if (n0 + wave * WN + j * 16 + 4 * g < N) {
-            float4 o;
-            o.x = (acc[i][j][0] * sav) * swv[j].x;
-            o.y = (acc[i][j][1] * sav) * swv[j].y;
-            o.z = (acc[i][j][2] * sav) * swv[j].z;
-            o.w = (acc[i][j][3] * sav) * swv[j].w;
-            *reinterpret_cast<float4*>(crow + j * 16) = o;
-          }
+      for (int j = 0; j < FB; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = t.n0 + WN * wave + 32 * j + 8 * q + 4 * h;
+          const uint32_t off = n < N ? (uint32_t)((32 * i + l32) * N + n) * 4u : kOutOfRange;
+          float4 o;
+          o.x = (acc[i][j][4 * q + 0] * sa[i]) * swv[j][q].x;
+          o.y = (acc[i][j][4 * q + 1] * sa[i]) * swv[j][q].y;
+          o.z = (acc[i][j][4 * q + 2] * sa[i]) * swv[j][q].z;
+          o.w = (acc[i][j][4 * q + 3] * sa[i]) * swv[j][q].w;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rsrc, off, 0, 0);
         }
+        acc[i][j] = floatx16{};
       }
     }
-    __syncthreads();   // the next tile's prologue overwrites stage 0 and a16[0]
   }
 }
 
-}  // namespace g4
+}  // namespace g5
 }  // namespace nvfp4moe
 
 using namespace nvfp4moe;
@@ -324,7 +436,7 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uin
                                                const uint8_t* w_bscales, const float* w_rscales,
                                                int64_t N, int64_t K, float* c, void* stream) {
   if (E < 1 || E > NVFP4MOE_MAX_EXPERTS || R_cap < 0) return NVFP4_ERR_SHAPE;
-  if (K <= 0 || K % g4::BK != 0 || K > 65536 || N < 16 || N % 16 != 0 || N > (1 << 24))
+  if (K <= 0 || K % g5::BK != 0 || K > 65536 || N < 16 || N % 16 != 0 || N > (1 << 20))
     return NVFP4_ERR_SHAPE;
   if (R_cap > INT32_MAX / 2 || (int64_t)E * N > INT32_MAX) return NVFP4_ERR_SHAPE;
   // the kernel addresses each operand with 32-bit byte offsets
@@ -337,14 +449,14 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uin
   if (!aligned16(a_codes) || !aligned16(a_bscales) || !aligned16(a_rscales) ||
       !aligned16(w_codes) || !aligned16(w_bscales) || !aligned16(w_rscales) || !aligned16(c))
     return NVFP4_ERR_ALIGN;
-  const int64_t n_tiles = (N + g4::BN - 1) / g4::BN;
-  const int64_t max_tiles = ((R_cap + g4::BM - 1) / g4::BM + E) * n_tiles;
+  const int64_t n_tiles = (N + g5::BN - 1) / g5::BN;
+  const int64_t max_tiles = ((R_cap + g5::BM - 1) / g5::BM + E) * n_tiles;
   if (max_tiles > INT32_MAX) return NVFP4_ERR_SHAPE;
-  // persistent grid: one workgroup (8 wavefronts) per CU on a 256-CU device, a multiple of 8
-  int64_t grid = max_tiles < 256 ? max_tiles : 256;
+  // persistent grid: two workgroups per CU on a 256-CU device, a multiple of 8
+  int64_t grid = max_tiles < 512 ? max_tiles : 512;
   if (grid >= 8) grid &= ~7ll;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  g4::grouped_gemm_kernel<<<(unsigned)grid, g4::kThreads, 0, s>>>(
+  g5::grouped_gemm_kernel<<<(unsigned)grid, g5::kThreads, 0, s>>>(
       a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales, (int)N,
       (int)K, c);
   return launch_status();
