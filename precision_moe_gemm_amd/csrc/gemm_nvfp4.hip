@@ -77,7 +77,9 @@ struct __align__(16) Stage {
 struct __align__(16) Smem {
   Stage st[kStages];
   uint8_t a16[2][BM * kA16Row];   // 2 x 16 KiB decoded activations (FP16)
-  int tile_start[NVFP4MOE_MAX_EXPERTS + 1];
+  float rs_a[BM];                 // row scales of the tile's rows (epilogue)
+  float rs_w[BN];                 // row scales of the tile's weight rows (directly after rs_a)
+  uint16_t tile_start[NVFP4MOE_MAX_EXPERTS + 1];   // m-tiles before expert e
 };
 
 // byte offset of 16-byte chunk c (0..7) of row r in the FP16 activation tile
@@ -144,13 +146,13 @@ struct Tile {
   int e, m0, rows, n0;
 };
 
-__device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_start, int E,
+__device__ __forceinline__ Tile tile_at(int L, int n_tiles, const uint16_t* tile_start, int E,
                                         const int32_t* __restrict__ offsets) {
   const int tm = L / n_tiles, tn = L - tm * n_tiles;
   int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (tile_start[mid] <= tm) lo = mid; else hi = mid;
+    if ((int)tile_start[mid] <= tm) lo = mid; else hi = mid;
   }
   // the values are the same in every lane: keep them in scalar registers
   Tile t;
@@ -185,15 +187,15 @@ void grouped_gemm_kernel(
         const int y = __shfl_up(incl, off, kWave);
         if (lane >= off) incl += y;
       }
-      if (e < E) sm.tile_start[e] = carry + incl - v;
+      if (e < E) sm.tile_start[e] = (uint16_t)(carry + incl - v);
       carry += __shfl(incl, kWave - 1, kWave);
     }
-    if (lane == 0) sm.tile_start[E] = carry;
+    if (lane == 0) sm.tile_start[E] = (uint16_t)carry;
   }
   __syncthreads();
 
   const int n_tiles = (N + BN - 1) / BN;
-  const int total = __builtin_amdgcn_readfirstlane(sm.tile_start[E]) * n_tiles;
+  const int total = __builtin_amdgcn_readfirstlane((int)sm.tile_start[E]) * n_tiles;
   // XCD-contiguous tile ranges when the grid is a multiple of 8 workgroups
   int begin, end, step;
   if ((gridDim.x & 7) == 0) {
@@ -367,10 +369,29 @@ void grouped_gemm_kernel(
   // epilogue stores are pending, whose completion order against loads is not
   // guaranteed); the barrier publishes them and the decoded activations of
   // this K-step, and frees the stage that the new loads go to.
-  auto run_tile = [&](auto full_tag, int fa_eff, bool after_stores) __attribute__((always_inline)) {
+  // Row scales of a tile for its epilogue, into LDS (issued at the top of the
+  // tile's last K-step, ahead of that step's loads, so that waiting for the
+  // loads counted in n_last also waits for these)
+  auto issue_rscales = [&](const Tile& t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = wave + 4 * u;        // 0,1 -> A rows, 2..5 -> W rows
+      if (q < 2)
+        lds_dma4(reinterpret_cast<const uint8_t*>(a_rscales),
+                 (uint32_t)min(t.m0 + 64 * q + lane, t.m0 + t.rows - 1) * 4u,
+                 reinterpret_cast<const uint8_t*>(sm.rs_a) + q * 256);
+      else if (q < 6)
+        lds_dma4(reinterpret_cast<const uint8_t*>(w_rscales),
+                 ((uint32_t)t.e * N + min(t.n0 + 64 * (q - 2) + lane, N - 1)) * 4u,
+                 reinterpret_cast<const uint8_t*>(sm.rs_a) + q * 256);
+    }
+  };
+
+  auto run_tile = [&](auto full_tag, int fa_eff, bool after_stores, const Tile& t) __attribute__((always_inline)) {
     for (int kt = 0; kt < nk; ++kt) {
       wait_vmcnt(kt == 0 && after_stores ? 0 : n_last);
       lds_barrier();
+      if (kt == nk - 1) issue_rscales(t);
       n_last = issue_loads(sm.st[sc]);
       mma_step(full_tag, fa_eff);
       sc = sc == kStages - 1 ? 0 : sc + 1;
@@ -381,42 +402,49 @@ void grouped_gemm_kernel(
   for (int L = begin; L < end; L += step) {
     const Tile t = tile_at(L, n_tiles, sm.tile_start, E, offsets);
     const int fa_eff = (t.rows + 31) >> 5;
-    if (fa_eff == FA) run_tile(std::true_type{}, FA, L != begin);
-    else run_tile(std::false_type{}, fa_eff, L != begin);
+    if (fa_eff == FA) run_tile(std::true_type{}, FA, L != begin, t);
+    else run_tile(std::false_type{}, fa_eff, L != begin, t);
 
     // epilogue: C = (acc * s_A[row]) * s_W[col].  Tile (i, j) of the lane
-    // holds row 32i + lane%32 and, for q = 0..3, columns 32j + 8q + 4h .. +3:
-    // 16-byte stores.  Rows past the tile's valid rows fall outside the
-    // buffer's range and are dropped by the hardware; columns past N get an
-    // out-of-range offset.  (The row scales are read here rather than ahead:
-    // kept in registers across the K-step they would not fit.)
+    // holds row 32i + lane%32, columns 32j + 8q + 4h .. +3 (q = 0..3).  Each
+    // 32 x 32 tile goes through a 4 KiB slice of the activation buffer that the
+    // last K-step read (16-byte chunks XOR-swizzled by row) and leaves as four
+    // stores of 8 rows x 128 contiguous bytes: whole cache lines.  Rows past
+    // the tile's valid rows fall outside the buffer's range and are dropped by
+    // the hardware; columns past N get an out-of-range offset.
+    wait_vmcnt(n_last);    // this wavefront's row-scale loads have landed
+    lds_barrier();         // everyone's, and nobody reads a16[ab ^ 1] any more
     float sa[FA];
-    float4 swv[FB][4];
 #pragma unroll
-    for (int i = 0; i < FA; ++i) sa[i] = a_rscales[t.m0 + min(32 * i + l32, t.rows - 1)];
-#pragma unroll
-    for (int j = 0; j < FB; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = t.n0 + WN * wave + 32 * j + 8 * q + 4 * h;
-        swv[j][q] = *reinterpret_cast<const float4*>(w_rscales + (int64_t)t.e * N + min(n, N - 4));
-      }
+    for (int i = 0; i < FA; ++i) sa[i] = sm.rs_a[32 * i + l32];
+    uint8_t* stg = sm.a16[ab ^ 1] + wave * 4096;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         c + (int64_t)t.m0 * N, (short)0, t.rows * N * 4, 0x00020000);
+    const int srow = lane >> 3, sch = lane & 7;   // store layout: 8 rows x 8 chunks per instruction
 #pragma unroll
-    for (int i = 0; i < FA; ++i) {
+    for (int j = 0; j < FB; ++j) {
+      float4 swv[4];
 #pragma unroll
-      for (int j = 0; j < FB; ++j) {
+      for (int q = 0; q < 4; ++q)
+        swv[q] = *reinterpret_cast<const float4*>(&sm.rs_w[WN * wave + 32 * j + 8 * q + 4 * h]);
+      const int n = t.n0 + WN * wave + 32 * j + 4 * sch;
+#pragma unroll
+      for (int i = 0; i < FA; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int n = t.n0 + WN * wave + 32 * j + 8 * q + 4 * h;
-          const uint32_t off = n < N ? (uint32_t)((32 * i + l32) * N + n) * 4u : kOutOfRange;
           float4 o;
-          o.x = (acc[i][j][4 * q + 0] * sa[i]) * swv[j][q].x;
-          o.y = (acc[i][j][4 * q + 1] * sa[i]) * swv[j][q].y;
-          o.z = (acc[i][j][4 * q + 2] * sa[i]) * swv[j][q].z;
-          o.w = (acc[i][j][4 * q + 3] * sa[i]) * swv[j][q].w;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rsrc, off, 0, 0);
+          o.x = (acc[i][j][4 * q + 0] * sa[i]) * swv[q].x;
+          o.y = (acc[i][j][4 * q + 1] * sa[i]) * swv[q].y;
+          o.z = (acc[i][j][4 * q + 2] * sa[i]) * swv[q].z;
+          o.w = (acc[i][j][4 * q + 3] * sa[i]) * swv[q].w;
+          *reinterpret_cast<float4*>(stg + l32 * 128 + (((2 * q + h) ^ (l32 & 7)) << 4)) = o;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 8 * r + srow;
+          const float4 v = *reinterpret_cast<const float4*>(stg + row * 128 + ((sch ^ (row & 7)) << 4));
+          const uint32_t off = n < N ? (uint32_t)((32 * i + row) * N + n) * 4u : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsrc, off, 0, 0);
         }
         acc[i][j] = floatx16{};
       }
