@@ -95,6 +95,23 @@ NVFP4MOE_API int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t K,
                                      void* stream);
 
 /*
+ * nvfp4_quantize_rows_tiled - the same quantisation as nvfp4_quantize_rows,
+ * written in the K-tiled layout that the grouped GEMM reads one contiguous
+ * block per K-step from (the scale layout conversion done by the quantiser
+ * itself; miniTE blog, "Two complementary interventions"):
+ *   codes   [rows/G][K/64][G][32]: byte b of slab kc of row r holds elements
+ *           64 kc + 2b (low nibble) and 64 kc + 2b + 1 of the row;
+ *   bscales [rows/G][K/64][G][4]:  the 4 block scales of slab kc;
+ *   rscales [rows] as in nvfp4_quantize_rows;
+ * with G = group_rows (for expert weights [E][N][K]: G = N).  Exactly the bytes
+ * of nvfp4_quantize_rows, moved.
+ * Requires K % 64 == 0, K <= NVFP4MOE_MAX_K, group_rows > 0, rows % group_rows == 0.
+ */
+NVFP4MOE_API int nvfp4_quantize_rows_tiled(const uint16_t* x, int64_t rows, int64_t K,
+                                           int64_t group_rows, uint8_t* codes,
+                                           uint8_t* bscales, float* rscales, void* stream);
+
+/*
  * nvfp4_quantize_permute - route, permute and quantise MoE activations in one
  * pass over x (the token amax is taken while the token is read for the
  * permutation).
@@ -133,17 +150,22 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
  * matrix cores with FP32 accumulation; the two FP32 row scales are applied in
  * the epilogue.  Error per element is within 2e-5 * sum_k |a_k w_k|.
  *   A (activations): a_codes [R_cap][K/2], a_bscales [R_cap][K/16], a_rscales [R_cap]
- *   W (weights):     w_codes [E][N][K/2], w_bscales [E][N][K/16], w_rscales [E][N]
+ *   W (weights), w_layout NVFP4_W_ROWMAJOR: w_codes [E][N][K/2], w_bscales [E][N][K/16];
+ *                w_layout NVFP4_W_KTILED:   w_codes [E][K/64][N][32], w_bscales [E][K/64][N][4]
+ *                (nvfp4_quantize_rows_tiled with group_rows = N); w_rscales [E][N]
  *   c                float [R_cap][N]; only rows < expert_offsets[E] are written
  * E = 1 with expert_offsets = {0, M} is a dense GEMM of M rows.
- * Requires K % 128 == 0, N % 16 == 0, N >= 16, K <= 65536, all pointers
- * 16-byte aligned.
+ * Requires K % 64 == 0, N % 16 == 0, 16 <= N <= 2^20, K <= 65536, all pointers
+ * 16-byte aligned.  Unknown w_layout: NVFP4_ERR_ARG.
  */
+#define NVFP4_W_ROWMAJOR 0
+#define NVFP4_W_KTILED 1
 NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_bscales,
                                     const float* a_rscales, const int32_t* expert_offsets,
                                     int32_t E, int64_t R_cap, const uint8_t* w_codes,
                                     const uint8_t* w_bscales, const float* w_rscales,
-                                    int64_t N, int64_t K, float* c, void* stream);
+                                    int64_t N, int64_t K, int32_t w_layout, float* c,
+                                    void* stream);
 
 /*
  * swiglu_quantize - weighted SwiGLU of the gate_up output with the amax taken

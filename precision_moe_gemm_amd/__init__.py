@@ -23,6 +23,8 @@ _LIB = None
 
 W_KN = 0
 W_NK = 1
+W_ROWMAJOR = 0   # NVFP4 weights [E, N, K/2] / [E, N, K/16]
+W_KTILED = 1     # NVFP4 weights [E, K/64, N, 32] / [E, K/64, N, 4]
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -52,7 +54,9 @@ SIGNATURES = {
     "nvfp4_quantize_rows": ([_P, _I64, _I64, _P, _P, _P, _P], _c.c_int),
     "nvfp4_quantize_permute": ([_P, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                                 _c.c_size_t, _P, _P], _c.c_int),
-    "nvfp4_grouped_gemm": ([_P, _P, _P, _P, _I32, _I64, _P, _P, _P, _I64, _I64, _P, _P], _c.c_int),
+    "nvfp4_quantize_rows_tiled": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], _c.c_int),
+    "nvfp4_grouped_gemm": ([_P, _P, _P, _P, _I32, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _P],
+                           _c.c_int),
     "swiglu_quantize": ([_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P, _P], _c.c_int),
     "unpermute_combine": ([_P, _I64, _I32, _I64, _P, _P, _P, _P], _c.c_int),
     "permute_gather_bf16": ([_P, _I64, _I64, _I32, _P, _I32, _P, _P, _P], _c.c_int),
@@ -135,6 +139,23 @@ def nvfp4_quantize_rows(x, codes=None, bscales=None, rscales=None):
     return codes, bscales, rscales
 
 
+def nvfp4_quantize_rows_tiled(x, group_rows: int, codes=None, bscales=None, rscales=None):
+    """x bf16 [rows, K] -> the K-tiled NVFP4 layout of groups of `group_rows` rows:
+    (codes u8 [rows/G, K/64, G, 32], bscales u8 [rows/G, K/64, G, 4], rscales f32 [rows])."""
+    _req(x, "x", _BF16, 2)
+    rows, K = x.shape
+    G = int(group_rows)
+    if G <= 0 or rows % G or K % 64:
+        raise ValueError("need rows % group_rows == 0 and K % 64 == 0")
+    codes = _empty((rows // G, K // 64, G, 32), torch.uint8, x) if codes is None else codes
+    bscales = _empty((rows // G, K // 64, G, 4), torch.uint8, x) if bscales is None else bscales
+    rscales = _empty((rows,), torch.float32, x) if rscales is None else rscales
+    _req(codes, "codes", _U8); _req(bscales, "bscales", _U8); _req(rscales, "rscales", _F32)
+    _check("nvfp4_quantize_rows_tiled", load_library().nvfp4_quantize_rows_tiled(
+        _ptr(x), rows, K, G, _ptr(codes), _ptr(bscales), _ptr(rscales), _stream()))
+    return codes, bscales, rscales
+
+
 def permute_workspace_size(T: int, k: int, E: int) -> int:
     return int(load_library().nvfp4moe_permute_workspace_size(T, k, E))
 
@@ -175,7 +196,9 @@ def nvfp4_quantize_permute(x, topk_ids, E: int, workspace=None, dev_err=None, ou
 
 def nvfp4_grouped_gemm(a_codes, a_bscales, a_rscales, expert_offsets, w_codes, w_bscales,
                        w_rscales, c=None):
-    """C[r] = A[r] W_e^T over expert-grouped rows.  W tensors [E, N, ...].  Returns C f32 [R_cap, N]."""
+    """C[r] = A[r] W_e^T over expert-grouped rows.  Returns C f32 [R_cap, N].
+    W in either layout: row-major codes [E, N, K/2] (bscales [E, N, K/16]) or
+    K-tiled codes [E, K/64, N, 32] (bscales [E, K/64, N, 4]); w_rscales [E, N]."""
     for t, n, d in ((a_codes, "a_codes", _U8), (a_bscales, "a_bscales", _U8),
                     (a_rscales, "a_rscales", _F32), (expert_offsets, "expert_offsets", _I32T),
                     (w_codes, "w_codes", _U8), (w_bscales, "w_bscales", _U8),
@@ -184,14 +207,19 @@ def nvfp4_grouped_gemm(a_codes, a_bscales, a_rscales, expert_offsets, w_codes, w
     R_cap = a_codes.shape[0]
     K = a_codes.shape[1] * 2
     E = expert_offsets.numel() - 1
-    N = w_codes.shape[1]
-    if w_codes.shape[0] != E or w_codes.shape[2] * 2 != K:
-        raise ValueError("w_codes must be [E, N, K/2] with the activations' K")
+    if w_codes.dim() == 4:
+        layout, N = W_KTILED, w_codes.shape[2]
+        ok = tuple(w_codes.shape) == (E, K // 64, N, 32) and tuple(w_bscales.shape) == (E, K // 64, N, 4)
+    else:
+        layout, N = W_ROWMAJOR, w_codes.shape[1]
+        ok = w_codes.dim() == 3 and w_codes.shape[0] == E and w_codes.shape[2] * 2 == K
+    if not ok:
+        raise ValueError("w_codes/w_bscales shapes do not match E, K and a known layout")
     c = _empty((R_cap, N), torch.float32, a_codes) if c is None else c
     _req(c, "c", _F32)
     _check("nvfp4_grouped_gemm", load_library().nvfp4_grouped_gemm(
         _ptr(a_codes), _ptr(a_bscales), _ptr(a_rscales), _ptr(expert_offsets), E, R_cap,
-        _ptr(w_codes), _ptr(w_bscales), _ptr(w_rscales), N, K, _ptr(c), _stream()))
+        _ptr(w_codes), _ptr(w_bscales), _ptr(w_rscales), N, K, layout, _ptr(c), _stream()))
     return c
 
 

@@ -168,7 +168,7 @@ void grouped_gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_bscales,
     const float* __restrict__ a_rscales, const int32_t* __restrict__ offsets, int E,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_bscales,
-    const float* __restrict__ w_rscales, int N, int K, float* __restrict__ c) {
+    const float* __restrict__ w_rscales, int N, int K, float* __restrict__ c, int w_tiled) {
   __shared__ Smem sm;
 
   const int tid = threadIdx.x, lane = lane_id();
@@ -222,22 +222,32 @@ void grouped_gemm_kernel(
   // rows (lane l -> row l/2, 16-byte half l%2) or 64 scale dwords.
   int lL = begin, lk = 0;
   uint32_t off_a, off_w[2], off_s[2];
+  // Weight K-step strides: row-major [E][N][K/2] moves 32 code bytes (4 scale
+  // bytes) along a row per K-step; the K-tiled layout [E][K/64][N][32] moves
+  // one whole slab of N rows, and a slab of 32 consecutive rows is 1 KiB of
+  // contiguous memory.
+  const uint32_t wstep_c = w_tiled ? (uint32_t)N * kRowB : (uint32_t)kRowB;
+  const uint32_t wstep_s = w_tiled ? (uint32_t)N * kScB : (uint32_t)kScB;
   auto set_load_tile = [&](int L) __attribute__((always_inline)) {
     const Tile t = tile_at(L, n_tiles, sm.tile_start, E, offsets);
     const int m_last = t.m0 + t.rows - 1;
     const int half = lane & 1;
     off_a = (uint32_t)min(t.m0 + 32 * wave + (lane >> 1), m_last) * kb + half * 16;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      off_w[u] = ((uint32_t)t.e * N + min(t.n0 + 64 * wave + 32 * u + (lane >> 1), N - 1)) * kb +
-                 half * 16;
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t n = (uint32_t)min(t.n0 + 64 * wave + 32 * u + (lane >> 1), N - 1);
+      off_w[u] = w_tiled ? ((uint32_t)t.e * nk * N + n) * kRowB + half * 16
+                         : ((uint32_t)t.e * N + n) * kb + half * 16;
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int q = wave + 4 * u;        // scale instruction: 0,1 -> A rows, 2..5 -> W rows
-      if (q < 2)
+      if (q < 2) {
         off_s[u] = (uint32_t)min(t.m0 + 64 * q + lane, m_last) * ks;
-      else
-        off_s[u] = ((uint32_t)t.e * N + min(t.n0 + 64 * (q - 2) + lane, N - 1)) * ks;
+      } else {
+        const uint32_t n = (uint32_t)min(t.n0 + 64 * (q - 2) + lane, N - 1);
+        off_s[u] = w_tiled ? ((uint32_t)t.e * nk * N + n) * kScB : ((uint32_t)t.e * N + n) * ks;
+      }
     }
   };
   // issues the loads of the cursor's K-step into stage S and advances the
@@ -245,13 +255,15 @@ void grouped_gemm_kernel(
   auto issue_loads = [&](Stage& S) __attribute__((always_inline)) -> int {
     if (lL >= end) return 0;
     const uint32_t ka = (uint32_t)lk * kRowB, kss = (uint32_t)lk * kScB;
+    const uint32_t kw = (uint32_t)lk * wstep_c, kws = (uint32_t)lk * wstep_s;
     lds_dma16(a_codes, ka + off_a, S.a + wave * 1024);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) lds_dma16(w_codes, ka + off_w[u], S.w + (2 * wave + u) * 1024);
+    for (int u = 0; u < 2; ++u) lds_dma16(w_codes, kw + off_w[u], S.w + (2 * wave + u) * 1024);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int q = wave + 4 * u;
-      if (q < 6) lds_dma4(q < 2 ? a_bscales : w_bscales, kss + off_s[u], S.as + q * 256);
+      if (q < 2) lds_dma4(a_bscales, kss + off_s[u], S.as + q * 256);
+      else if (q < 6) lds_dma4(w_bscales, kws + off_s[u], S.as + q * 256);
     }
     if (++lk == nk) {
       lk = 0;
@@ -462,7 +474,9 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uin
                                                const int32_t* expert_offsets, int32_t E,
                                                int64_t R_cap, const uint8_t* w_codes,
                                                const uint8_t* w_bscales, const float* w_rscales,
-                                               int64_t N, int64_t K, float* c, void* stream) {
+                                               int64_t N, int64_t K, int32_t w_layout, float* c,
+                                               void* stream) {
+  if (w_layout != NVFP4_W_ROWMAJOR && w_layout != NVFP4_W_KTILED) return NVFP4_ERR_ARG;
   if (E < 1 || E > NVFP4MOE_MAX_EXPERTS || R_cap < 0) return NVFP4_ERR_SHAPE;
   if (K <= 0 || K % g5::BK != 0 || K > 65536 || N < 16 || N % 16 != 0 || N > (1 << 20))
     return NVFP4_ERR_SHAPE;
@@ -486,6 +500,6 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uin
   hipStream_t s = static_cast<hipStream_t>(stream);
   g5::grouped_gemm_kernel<<<(unsigned)grid, g5::kThreads, 0, s>>>(
       a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales, (int)N,
-      (int)K, c);
+      (int)K, c, (int)(w_layout == NVFP4_W_KTILED));
   return launch_status();
 }

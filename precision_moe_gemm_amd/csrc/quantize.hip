@@ -121,6 +121,34 @@ __device__ __forceinline__ void store_row(const RowCodes<NCH>& o, const uint32_t
   if (lane == 0) rscales[row] = o.s;
 }
 
+// Writes one quantised row in the K-tiled layout of a group of G rows:
+// codes [rows/G][K/64][G][32 B], block scales [rows/G][K/64][G][4 B].  The 64
+// elements of K-slab kc of a row are its 32 code bytes and its 4 block scales,
+// so the slab of G consecutive rows is one contiguous block (what the grouped
+// GEMM reads per K-step).  Requires K % 64 == 0.
+template <int NCH>
+__device__ __forceinline__ void store_row_tiled(const RowCodes<NCH>& o,
+                                               const uint32_t (&sw)[(NCH + 7) / 8], int K,
+                                               int64_t row, int64_t G, uint8_t* __restrict__ codes,
+                                               uint8_t* __restrict__ bscales,
+                                               float* __restrict__ rscales) {
+  const int lane = lane_id();
+  const int64_t g = row / G, rr = row - g * G;
+  const int64_t slab0 = g * (int64_t)(K >> 6);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int base = c * kChunk + lane * 8;
+    if (base < K)
+      *reinterpret_cast<uint32_t*>(codes + ((slab0 + (base >> 6)) * G + rr) * 32 + ((base & 63) >> 1)) = o.q[c];
+  }
+#pragma unroll
+  for (int r = 0; r < (NCH + 7) / 8; ++r) {
+    const int w = r * 64 + lane;
+    if (w * 64 < K) *reinterpret_cast<uint32_t*>(bscales + ((slab0 + w) * G + rr) * 4) = sw[r];
+  }
+  if (lane == 0) rscales[row] = o.s;
+}
+
 template <int NCH>
 __device__ __forceinline__ void pack_scales(const RowCodes<NCH>& o, uint32_t (&sw)[(NCH + 7) / 8]) {
 #pragma unroll
@@ -171,6 +199,21 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
   uint32_t sw[(NCH + 7) / 8];
   pack_scales<NCH>(o, sw);
   store_row<NCH>(o, sw, K, row, codes, bscales, rscales);
+}
+
+template <int NCH>
+__global__ __launch_bounds__(256) void quantize_rows_tiled_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int K, int64_t G, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ bscales, float* __restrict__ rscales) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float v[NCH][8];
+  load_bf16_row<NCH>(x + row * (int64_t)K, K, v);
+  RowCodes<NCH> o;
+  quantize_lane_row<NCH>(v, o);
+  uint32_t sw[(NCH + 7) / 8];
+  pack_scales<NCH>(o, sw);
+  store_row_tiled<NCH>(o, sw, K, row, G, codes, bscales, rscales);
 }
 
 // Each wavefront reads and quantises kTPW tokens (t, t + W, ... for W
@@ -639,6 +682,22 @@ NVFP4MOE_API int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t K,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   NVFP4_DISPATCH_NCH(K, quantize_rows_kernel, grid, s, x, rows, (int)K, codes, bscales, rscales);
+  return launch_status();
+}
+
+NVFP4MOE_API int nvfp4_quantize_rows_tiled(const uint16_t* x, int64_t rows, int64_t K,
+                                           int64_t group_rows, uint8_t* codes, uint8_t* bscales,
+                                           float* rscales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 64 != 0 || K > NVFP4MOE_MAX_K) return NVFP4_ERR_SHAPE;
+  if (group_rows <= 0 || rows % group_rows != 0) return NVFP4_ERR_SHAPE;
+  if (rows == 0) return NVFP4_OK;
+  if (!x || !codes || !bscales || !rscales) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(bscales) || !aligned16(rscales))
+    return NVFP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  NVFP4_DISPATCH_NCH(K, quantize_rows_tiled_kernel, grid, s, x, rows, (int)K, group_rows, codes,
+                     bscales, rscales);
   return launch_status();
 }
 

@@ -49,6 +49,23 @@ def quantize_weights_gpu(w_bits: np.ndarray):
     return c.view(E, N, K // 2), b.view(E, N, K // 16), s.view(E, N)
 
 
+def quantize_weights_gpu_tiled(w_bits: np.ndarray):
+    """[E, N, K] bf16 bits -> K-tiled NVFP4 on the device (codes [E, K/64, N, 32],
+    bscales [E, K/64, N, 4], rscales [E, N])."""
+    E, N, K = w_bits.shape
+    c, b, s = pmg.nvfp4_quantize_rows_tiled(bf16_dev(w_bits.reshape(E * N, K)), N)
+    return c, b, s.view(E, N)
+
+
+def ktile(codes: np.ndarray, bscales: np.ndarray):
+    """Row-major NVFP4 [G, R, K/2] / [G, R, K/16] -> the K-tiled layout
+    [G, K/64, R, 32] / [G, K/64, R, 4] (a pure move of bytes)."""
+    G, R, half = codes.shape
+    kt = half // 32
+    return (codes.reshape(G, R, kt, 32).transpose(0, 2, 1, 3).copy(),
+            bscales.reshape(G, R, kt, 4).transpose(0, 2, 1, 3).copy())
+
+
 def assert_within(got: np.ndarray, ref: np.ndarray, bound: np.ndarray, what: str = ""):
     err = np.abs(got.astype(np.float64) - ref)
     bad = err > bound

@@ -81,8 +81,11 @@ def test_gemm_host_checks(lib):
     f = lib.nvfp4_grouped_gemm
     base = dict(E=128, R=32768, N=1536, K=2048)
     call = lambda **kw: f(FAKE, FAKE, FAKE, FAKE, kw.get("E", 128), kw.get("R", 32768), FAKE, FAKE,
-                          kw.get("wr", FAKE), kw.get("N", 1536), kw.get("K", 2048), kw.get("c", FAKE), None)
-    assert call(K=2000) == ERR_SHAPE                        # K % 128
+                          kw.get("wr", FAKE), kw.get("N", 1536), kw.get("K", 2048), kw.get("lay", 0),
+                          kw.get("c", FAKE), None)
+    assert call(K=2000) == ERR_SHAPE                        # K % 64
+    assert call(N=(1 << 20) + 16) == ERR_SHAPE
+    assert call(lay=2) == ERR_ARG
     assert call(N=1537) == ERR_SHAPE
     assert call(E=0) == ERR_SHAPE
     assert call(c=None) == ERR_NULL
@@ -90,6 +93,16 @@ def test_gemm_host_checks(lib):
     g = lib.bf16_grouped_gemm
     assert g(FAKE, FAKE, 128, 32768, FAKE, 7, 768, 2048, FAKE, None) == ERR_ARG
     assert g(FAKE, FAKE, 128, 32768, FAKE, 0, 768, 2040, FAKE, None) == ERR_SHAPE
+
+
+def test_quantize_rows_tiled_host_checks(lib):
+    f = lib.nvfp4_quantize_rows_tiled
+    assert f(FAKE, 8, 96, 4, FAKE, FAKE, FAKE, None) == ERR_SHAPE     # K % 64
+    assert f(FAKE, 8, 128, 3, FAKE, FAKE, FAKE, None) == ERR_SHAPE    # rows % group_rows
+    assert f(FAKE, 8, 128, 0, FAKE, FAKE, FAKE, None) == ERR_SHAPE
+    assert f(None, 8, 128, 4, FAKE, FAKE, FAKE, None) == ERR_NULL
+    assert f(FAKE, 8, 128, 4, FAKE + 4, FAKE, FAKE, None) == ERR_ALIGN
+    assert f(None, 0, 128, 4, None, None, None, None) == OK
 
 
 def test_streaming_ops_host_checks(lib):

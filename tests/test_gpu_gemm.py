@@ -13,7 +13,7 @@ import precision_moe_gemm_amd as pmg
 import workloads as W
 from oracle import gemm as og, layer as ol, permute as op, quantize as oq
 from helpers import (assert_within, bf16_dev, dev, host, gpu_ready, quantize_weights_gpu,
-                     quantize_weights_oracle, sample_rows)
+                     quantize_weights_gpu_tiled, quantize_weights_oracle, sample_rows)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_ready(), reason="needs a GPU")]
@@ -38,11 +38,15 @@ def _routed_case(T, H, E, k, N, kind, seed):
     ids, _ = W.make_routing(kind, T, E, k, seed)
     w_bits = W.gaussian_bf16((E, N, H), 0.02, seed, 20)
     res = pmg.nvfp4_quantize_permute(bf16_dev(x), dev(ids), E)
-    w = quantize_weights_gpu(w_bits)
-    c = pmg.nvfp4_grouped_gemm(res["codes"], res["bscales"], res["rscales"], res["expert_offsets"], *w)
-    torch.cuda.synchronize()
+    a = (res["codes"], res["bscales"], res["rscales"], res["expert_offsets"])
+    c = host(pmg.nvfp4_grouped_gemm(*a, *quantize_weights_gpu(w_bits)))
+    # the K-tiled weight layout is the same computation on moved bytes
     (off, r2t, t2r), a_ref = ol.quantize_permute_ref(x, ids, E)
-    return host(c), off, a_ref, w_bits
+    if H % 64 == 0:
+        ct = host(pmg.nvfp4_grouped_gemm(*a, *quantize_weights_gpu_tiled(w_bits)))
+        R = int(off[-1])
+        assert np.array_equal(ct[:R], c[:R]), "K-tiled weights change the result"
+    return c, off, a_ref, w_bits
 
 
 @pytest.mark.parametrize("T,H,E,k,N,kind", [

@@ -10,7 +10,7 @@ import torch
 import precision_moe_gemm_amd as pmg
 import workloads as W
 from oracle import layer as ol, permute as op, quantize as oq
-from helpers import bf16_dev, dev, host, gpu_ready
+from helpers import bf16_dev, dev, host, gpu_ready, ktile
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_ready(), reason="needs a GPU")]
@@ -38,6 +38,20 @@ def test_quantize_rows_tiny_config():
 @pytest.mark.parametrize("K", [16, 48, 256, 512, 528, 768, 1040, 2048, 4096, 8192])
 def test_quantize_rows_lengths(K):
     _check_rows(W.activations(37, K, config=2, tensor=K), f"K={K}")
+
+
+@pytest.mark.parametrize("rows,K,G", [(12, 64, 12), (256, 2048, 128), (6, 8192, 2), (40, 768, 8)])
+def test_quantize_rows_tiled_is_the_oracle_in_the_tiled_layout(rows, K, G):
+    """K-tiled output = the oracle's row-major codes and scales, bytes moved."""
+    print(f"[quantize_rows_tiled] rows={rows} K={K} G={G}", flush=True)
+    bits = W.activations(rows, K, config=3, tensor=K + G)
+    c, b, s = pmg.nvfp4_quantize_rows_tiled(bf16_dev(bits), G)
+    torch.cuda.synchronize()
+    rc, rb, rs = oq.quantize_rows_bf16(bits)
+    tc, tb = ktile(rc.reshape(rows // G, G, K // 2), rb.reshape(rows // G, G, K // 16))
+    assert np.array_equal(host(c), tc)
+    assert np.array_equal(host(b), tb)
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
 
 
 def test_quantize_rows_edge_values():
