@@ -72,7 +72,7 @@ typedef enum nvfp4_status {
   NVFP4_ERR_ARG = 6        /* an enumerated argument has an unknown value */
 } nvfp4_status;
 
-#define NVFP4_DEVERR_BAD_EXPERT 1
+#define NVFP4_DEVERR_BAD_EXPERT 1   /* an expert id outside [0, E): that entry takes no row */
 
 /* Text for a status code (static storage, never NULL). */
 NVFP4MOE_API const char* nvfp4moe_status_string(int status);

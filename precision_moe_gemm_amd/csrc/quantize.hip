@@ -17,6 +17,7 @@
 // contiguous bytes; four block scales pack into one word.
 #include "common.h"
 
+#include <algorithm>
 #include <atomic>
 #include <random>
 
@@ -216,176 +217,7 @@ __global__ __launch_bounds__(256) void quantize_rows_tiled_kernel(
   store_row_tiled<NCH>(o, sw, K, row, G, codes, bscales, rscales);
 }
 
-// Each wavefront reads and quantises kTPW tokens (t, t + W, ... for W
-// wavefronts in the grid), issuing the loads of all of them before the first
-// is processed; a token is quantised once and its bytes are written to each
-// of its k routed rows.  One token per wavefront measured fastest: the more
-// wavefronts, the more loads in flight.
-constexpr int kTPW = 1;
-
-template <int NCH>
-__global__ __launch_bounds__(256) void quantize_scatter_kernel(
-    const uint16_t* __restrict__ x, int64_t T, int K, int k, const int32_t* __restrict__ tk_to_row,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales, float* __restrict__ rscales) {
-  const int64_t wid = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  const int64_t nw = (int64_t)gridDim.x * kRowsPerBlock;
-  const int lane = lane_id();
-  uint4 raw[kTPW][NCH];
-  int my_row[kTPW];
-#pragma unroll
-  for (int j = 0; j < kTPW; ++j) {
-    const int64_t t = wid + j * nw;
-    if (t < T) {
-      load_bf16_raw<NCH>(x + t * (int64_t)K, K, raw[j]);
-      my_row[j] = lane < k ? tk_to_row[t * k + lane] : -1;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < kTPW; ++j) {
-    const int64_t t = wid + j * nw;
-    if (t >= T) break;
-    float v[NCH][8];
-    unpack_bf16<NCH>(raw[j], v);
-    RowCodes<NCH> o;
-    quantize_lane_row<NCH>(v, o);
-    uint32_t sw[(NCH + 7) / 8];
-    pack_scales<NCH>(o, sw);
-    for (int slot = 0; slot < k; ++slot) {
-      const int row = __shfl(my_row[j], slot, kWave);
-      if (row >= 0) store_row<NCH>(o, sw, K, row, codes, bscales, rscales);
-    }
-  }
-}
-
-// Per-chunk expert histogram (counts are order-free, so LDS atomics are fine).
-__global__ __launch_bounds__(kRouteThreads) void route_hist_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int32_t* __restrict__ chunk_hist,
-    int32_t* __restrict__ dev_err) {
-  __shared__ int32_t h[NVFP4MOE_MAX_EXPERTS];
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) h[e] = 0;
-  __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kRouteChunk;
-  bool bad = false;
-  for (int i = threadIdx.x; i < kRouteChunk; i += kRouteThreads) {
-    const int64_t idx = base + i;
-    if (idx < n) {
-      const int e = ids[idx];
-      if (e >= 0 && e < E) atomicAdd(&h[e], 1);
-      else bad = true;
-    }
-  }
-  if (bad && dev_err) atomicOr(dev_err, NVFP4_DEVERR_BAD_EXPERT);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) chunk_hist[(int64_t)blockIdx.x * E + e] = h[e];
-}
-
-// Offsets, and the stable rank of every routing entry of this chunk: row =
-// offsets[e] + (entries of e in earlier chunks) + (earlier entries of e in
-// this chunk).  Wavefront w ranks the chunk's entries [256w, 256w+256) in
-// order, 64 at a time: lanes with the same expert find each other with one
-// ballot per bit of the expert id, and a per-wavefront counter per expert
-// carries the count to the next 64.  The wavefronts' counts are then
-// prefix-summed per expert, which orders the whole chunk.
-__global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int nchunks,
-    const int32_t* __restrict__ chunk_hist, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ row_to_tk, int32_t* __restrict__ tk_to_row) {
-  constexpr int kW = kRouteThreads / kWave;            // 4 wavefronts
-  constexpr int kPerWave = kRouteChunk / kW;           // 256 entries each
-  __shared__ int32_t base[NVFP4MOE_MAX_EXPERTS];
-  __shared__ int32_t tot[NVFP4MOE_MAX_EXPERTS];
-  __shared__ int32_t wcnt[kW][NVFP4MOE_MAX_EXPERTS];
-  const int c = blockIdx.x;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
-    // 16 independent loads in flight per batch (a plain loop would wait for
-    // each load before issuing the next)
-    int t = 0, pre = 0;
-    for (int j0 = 0; j0 < nchunks; j0 += 16) {
-      int v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        v[u] = (j0 + u < nchunks) ? chunk_hist[(int64_t)(j0 + u) * E + e] : 0;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        t += v[u];
-        pre += (j0 + u < c) ? v[u] : 0;
-      }
-    }
-    tot[e] = t;
-    base[e] = pre;
-#pragma unroll
-    for (int w = 0; w < kW; ++w) wcnt[w][e] = 0;
-  }
-  __syncthreads();
-  // ranks inside this wavefront's 256 entries (no barrier needed: one wavefront
-  // owns wcnt[wave][*] and executes its LDS accesses in order)
-  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  int rank[kPerWave / kWave], ex[kPerWave / kWave];
-#pragma unroll
-  for (int sub = 0; sub < kPerWave / kWave; ++sub) {
-    const int64_t idx = (int64_t)c * kRouteChunk + wave * kPerWave + sub * kWave + lane;
-    const int e = idx < n ? ids[idx] : -1;
-    const bool valid = idx < n && e >= 0 && e < E;
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t bb = __ballot(bit);
-      peers &= bit ? bb : ~bb;
-    }
-    const int r = __popcll(peers & lt_mask);
-    int before = 0;
-    if (valid) before = wcnt[wave][e];
-    if (valid && r == 0) wcnt[wave][e] = before + __popcll(peers);
-    rank[sub] = before + r;
-    ex[sub] = valid ? e : -1;
-  }
-  __syncthreads();
-  // per expert: offsets (exclusive scan of totals, wavefront 0) and the
-  // prefix of the wavefront counts
-  if (wave == 0) {
-    int carry = 0;
-    for (int e0 = 0; e0 < E; e0 += kWave) {
-      const int e = e0 + lane;
-      const int v = e < E ? tot[e] : 0;
-      int incl = v;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += y;
-      }
-      if (e < E) {
-        base[e] += carry + incl - v;
-        if (c == 0) offsets[e] = carry + incl - v;
-      }
-      carry += __shfl(incl, kWave - 1, kWave);
-    }
-    if (c == 0 && lane == 0) offsets[E] = carry;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
-    int acc = base[e];
-#pragma unroll
-    for (int w = 0; w < kW; ++w) {
-      const int v = wcnt[w][e];
-      wcnt[w][e] = acc;
-      acc += v;
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int sub = 0; sub < kPerWave / kWave; ++sub) {
-    const int64_t idx = (int64_t)c * kRouteChunk + wave * kPerWave + sub * kWave + lane;
-    if (idx >= n) continue;
-    const int e = ex[sub];
-    const int row = e >= 0 ? wcnt[wave][e] + rank[sub] : -1;
-    tk_to_row[idx] = row;
-    if (e >= 0) row_to_tk[row] = (int32_t)idx;
-  }
-}
-
-// ------------------------------------------------------------------ two-kernel route
+// ------------------------------------------------------------------ many-workgroup route plan
 // Plan: workgroup c counts chunk c (1024 routing entries) per expert and
 // publishes the counts; the last workgroup to arrive scans them over chunks
 // and experts and writes, in place,
@@ -569,6 +401,188 @@ __global__ __launch_bounds__(256) void quantize_route_kernel(
   }
 }
 
+// Route + permute + quantise in two launches.
+//
+// The plan: one workgroup reads the whole routing list once and counts it per
+// (4096-entry chunk, expert) in LDS, then writes
+//   base[c][e] = offsets[e] + (entries of e in chunks before c)
+// and the expert offsets.  One workgroup keeps every count on chip: no
+// global round trips between the steps.  Used while nchunks * E <= kPlanLds.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanChunkLog = 12;        // 4096 routing entries per plan chunk
+constexpr int kPlanLds = 16384;          // ints of LDS for the (chunk, expert) counts
+
+inline int plan_chunks(int64_t n) { return n > 0 ? (int)((n + (1 << kPlanChunkLog) - 1) >> kPlanChunkLog) : 1; }
+
+__global__ __launch_bounds__(kPlanThreads) void route_plan1_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int nchunks, int32_t* __restrict__ base,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ dev_err) {
+  __shared__ int32_t cnt[kPlanLds];
+  __shared__ int32_t tot[NVFP4MOE_MAX_EXPERTS];
+  __shared__ int32_t wsum[kPlanThreads / kWave];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  for (int i = tid; i < nchunks * E; i += kPlanThreads) cnt[i] = 0;
+  __syncthreads();
+  bool bad = false;
+  const bool vec = (reinterpret_cast<uintptr_t>(ids) & 15) == 0;
+  for (int i0 = 4 * tid; i0 < n; i0 += 4 * kPlanThreads * 4) {
+    int4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 4 * kPlanThreads;
+      if (vec && i + 3 < n) {
+        q[u] = *reinterpret_cast<const int4*>(ids + i);
+      } else {
+        q[u].x = i < n ? ids[i] : -1;
+        q[u].y = i + 1 < n ? ids[i + 1] : -1;
+        q[u].z = i + 2 < n ? ids[i + 2] : -1;
+        q[u].w = i + 3 < n ? ids[i + 3] : -1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 4 * kPlanThreads;
+      const int v[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (i + c >= n) continue;
+        const int e = v[c];
+        if (e >= 0 && e < E) atomicAdd(&cnt[((i + c) >> kPlanChunkLog) * E + e], 1);
+        else bad = true;
+      }
+    }
+  }
+  if (bad && dev_err) atomicOr(dev_err, NVFP4_DEVERR_BAD_EXPERT);
+  __syncthreads();
+  // per expert: exclusive prefix over chunks, in place, and the total
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int acc = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = cnt[c * E + e];
+      cnt[c * E + e] = acc;
+      acc += v;
+    }
+    tot[e] = acc;
+  }
+  __syncthreads();
+  // exclusive scan of the totals over experts: per wavefront, then across
+  const int v = tid < E ? tot[tid] : 0;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  if (tid < E) tot[tid] = before + incl - v;
+  if (tid == kPlanThreads - 1) offsets[E] = before + incl;
+  __syncthreads();
+  for (int e = tid; e < E; e += kPlanThreads) offsets[e] = tot[e];
+  for (int i = tid; i < nchunks * E; i += kPlanThreads) base[i] = cnt[i] + tot[i % E];
+}
+
+// The main pass.  Workgroup w (8 wavefronts) owns tokens [8w, 8w + 8), one
+// per wavefront.  Its activations and every routing id it needs (its own
+// entries, and its chunk's entries before them, at most 4095) are loaded at
+// the start.  It counts per expert the chunk's entries before its first one,
+// ranks its own entries in (token, slot) order by ballot matching, and turns
+// (chunk, expert, rank) into rows with the plan's bases.  Each token is
+// quantised once and written to its k rows.
+constexpr int kQpWaves = 8;
+constexpr int kQpThreads = kQpWaves * 64;
+constexpr int kQpPre = (1 << kPlanChunkLog) / kQpThreads;   // prefix ids per thread (8)
+
+template <int NCH>
+__global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
+    const uint16_t* __restrict__ x, int64_t T, int K, const int32_t* __restrict__ ids, int k, int E,
+    const int32_t* __restrict__ base, uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales,
+    float* __restrict__ rscales, int32_t* __restrict__ row_to_tk, int32_t* __restrict__ tk_to_row) {
+  __shared__ int32_t pre[2][NVFP4MOE_MAX_EXPERTS];
+  __shared__ int32_t rows[kQpWaves * NVFP4MOE_MAX_TOPK];
+  const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * kQpWaves + wave;
+  const int n = (int)(T * k);
+  const int e0 = (int)((int64_t)blockIdx.x * kQpWaves * k);       // first entry of the group
+  const int e1 = min(e0 + kQpWaves * k, n);                        // one past the last
+  const int cs = (e0 >> kPlanChunkLog) << kPlanChunkLog;          // start of e0's chunk
+  const int second = cs + (1 << kPlanChunkLog);                    // start of the next chunk
+
+  uint4 raw[NCH];
+  if (t < T) load_bf16_raw<NCH>(x + t * (int64_t)K, K, raw);
+  // the chunk's ids before e0 (strided over the workgroup) and, in wavefront
+  // 0, the group's own ids
+  int pv[kQpPre];
+#pragma unroll
+  for (int u = 0; u < kQpPre; ++u) {
+    const int i = cs + u * kQpThreads + tid;
+    pv[u] = i < e0 ? ids[i] : -1;
+  }
+  int own[(kQpWaves * NVFP4MOE_MAX_TOPK) / kWave];
+#pragma unroll
+  for (int u = 0; u < (kQpWaves * NVFP4MOE_MAX_TOPK) / kWave; ++u) {
+    const int idx = e0 + u * kWave + lane;
+    own[u] = (wave == 0 && idx < e1) ? ids[idx] : -1;
+  }
+
+  for (int e = tid; e < E; e += kQpThreads) { pre[0][e] = 0; pre[1][e] = 0; }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kQpPre; ++u) {
+    const int e = pv[u];
+    if (e >= 0 && e < E) atomicAdd(&pre[0][e], 1);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+#pragma unroll
+    for (int u = 0; u < (kQpWaves * NVFP4MOE_MAX_TOPK) / kWave; ++u) {
+      const int i0 = e0 + u * kWave;
+      if (i0 >= e1) break;
+      const int idx = i0 + lane;
+      const int e = own[u];
+      const bool valid = idx < e1 && e >= 0 && e < E;
+      const int part = idx >= second ? 1 : 0;
+      uint64_t peers = __ballot(valid);
+      const uint64_t pb = __ballot(valid && part);
+      peers &= part ? pb : ~pb;
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t bb = __ballot(bit);
+        peers &= bit ? bb : ~bb;
+      }
+      const int r = __popcll(peers & lt_mask);
+      int row = -1;
+      if (valid) {
+        const int before = pre[part][e];
+        row = base[(idx >> kPlanChunkLog) * E + e] + before + r;
+        if (r == 0) pre[part][e] = before + __popcll(peers);
+      }
+      if (idx < e1) {
+        tk_to_row[idx] = row;
+        rows[idx - e0] = row;
+        if (valid) row_to_tk[row] = idx;
+      }
+    }
+  }
+  __syncthreads();
+  if (t >= T) return;
+  float v[NCH][8];
+  unpack_bf16<NCH>(raw, v);
+  RowCodes<NCH> o;
+  quantize_lane_row<NCH>(v, o);
+  uint32_t sw[(NCH + 7) / 8];
+  pack_scales<NCH>(o, sw);
+  const int my_row = lane < k ? rows[wave * k + lane] : -1;
+  for (int slot = 0; slot < k; ++slot) {
+    const int row = __shfl(my_row, slot, kWave);
+    if (row >= 0) store_row<NCH>(o, sw, K, row, codes, bscales, rscales);
+  }
+}
+
 // Weighted SwiGLU on one routed row, evaluated in FP64 and rounded once to
 // FP32, then the row quantiser; the amax is taken on the values just made.
 template <int NCH>
@@ -723,8 +737,27 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
   const int nchunks = (int)route_chunks(T, k);
   unsigned long long* arrivals = static_cast<unsigned long long*>(workspace);
   int32_t* table = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + kPlanArrivalBytes);
-  if (k * kRowsPerBlock <= kRouteChunk) {
-    // plan (offsets + per-chunk bases), then rank + quantise + scatter
+  const int pchunks = plan_chunks(n);
+  if ((int64_t)pchunks * E <= kPlanLds && n <= INT32_MAX / 2 && H <= 4096) {
+    // plan in one workgroup, then rank + quantise + scatter
+    route_plan1_kernel<<<1, kPlanThreads, 0, s>>>(topk_ids, (int)n, E, pchunks, table,
+                                                  expert_offsets, dev_err);
+    if (T > 0) {
+      const unsigned grid = (unsigned)((T + kQpWaves - 1) / kQpWaves);
+      switch (nch_for(H)) {
+#define QP_LAUNCH(C)                                                                           \
+        case C:                                                                                \
+          quantize_permute_kernel<C><<<grid, kQpThreads, 0, s>>>(x, T, (int)H, topk_ids, (int)k, \
+              (int)E, table, codes, bscales, rscales, row_to_tk, tk_to_row);                   \
+          break;
+        QP_LAUNCH(1) QP_LAUNCH(2) QP_LAUNCH(4)
+        default: QP_LAUNCH(8)
+#undef QP_LAUNCH
+      }
+    }
+  } else {
+    // long routing lists or long rows: plan over chunks of 1024 entries in many
+    // workgroups (the last to arrive scans), then rank + quantise + scatter
     route_plan_kernel<<<nchunks, kRouteThreads, 0, s>>>(topk_ids, n, E, nchunks, arrivals,
                                                         next_call_tag(), table, expert_offsets,
                                                         dev_err);
@@ -732,16 +765,6 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
       const dim3 grid((unsigned)((T + kRowsPerBlock - 1) / kRowsPerBlock));
       NVFP4_DISPATCH_NCH(H, quantize_route_kernel, grid, s, x, T, (int)H, topk_ids, (int)k, (int)E,
                          table, codes, bscales, rscales, row_to_tk, tk_to_row);
-    }
-  } else {
-    // long routing lists: per-chunk histograms, ranks, then quantise + scatter
-    route_hist_kernel<<<nchunks, kRouteThreads, 0, s>>>(topk_ids, n, E, table, dev_err);
-    route_scatter_kernel<<<nchunks, kRouteThreads, 0, s>>>(topk_ids, n, E, nchunks, table,
-                                                           expert_offsets, row_to_tk, tk_to_row);
-    if (T > 0) {
-      const dim3 grid((unsigned)((T + kRowsPerBlock * kTPW - 1) / (kRowsPerBlock * kTPW)));
-      NVFP4_DISPATCH_NCH(H, quantize_scatter_kernel, grid, s, x, T, (int)H, (int)k, tk_to_row,
-                         codes, bscales, rscales);
     }
   }
   return launch_status();

@@ -110,12 +110,20 @@ def test_quantize_permute_full_config():
 @pytest.mark.parametrize("T,E,k,kind", [(5, 4, 2, "uniform"), (1, 1, 1, "uniform"), (1, 128, 8, "uniform"),
                                           (1000, 128, 8, "zipf"), (777, 16, 3, "uniform"),
                                           (2049, 64, 8, "softmax"), (300, 1, 1, "uniform"),
-                                          (128, 1024, 32, "uniform"),   # E > 512: chunked routing
-                                          (40000, 128, 8, "zipf")])     # > 2^18 entries: chunked routing
+                                          (128, 1024, 32, "uniform"),   # E > 512
+                                          (40000, 128, 8, "zipf"),      # 320k entries, one-workgroup plan
+                                          (3000, 1024, 32, "uniform")]) # 96k entries x 1024 experts: many-workgroup plan
 def test_quantize_permute_ragged(T, E, k, kind):
     x = W.activations(T, 64 if T > 10000 else 256, config=9, tensor=T)
     ids, _ = W.make_routing(kind, T, E, k, config=9)
     _check_permute(x, ids, E, f"{kind}")
+
+
+def test_quantize_permute_long_rows():
+    """H > 4096 takes the many-workgroup plan and the 1-token-per-wavefront pass."""
+    x = W.activations(50, 8192, config=9, tensor=3)
+    ids, _ = W.make_routing("uniform", 50, 16, 4, config=9)
+    _check_permute(x, ids, 16, "H=8192")
 
 
 def test_quantize_permute_empty_experts_and_zero_tokens():
