@@ -43,11 +43,49 @@ def parse():
     p.add_argument("--routing", default="softmax", choices=["softmax", "uniform", "zipf"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle sample's CPU time")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only copy MIB MiB device to device 4 times (calibrates the HBM byte counters)")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_hbm_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "precision_moe_gemm_amd", "csrc", "gemm_nvfp4.hip")
+
+
+def measured_traffic():
+    """HBM bytes per gate_up launch from the committed counter summary, if it was
+    taken on the kernel source as it is now (else None)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+        src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic:"):
+            kv = dict(item.split("=", 1) for item in line[len("traffic:"):].split())
+            if kv.get("gemm_source_sha256") == src:
+                return int(kv["fetch_bytes"]) + int(kv["write_bytes"])
+    return None
+
+
+def copy_probe(mib: int):
+    import torch
+    n = mib * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_copy": n * 4}), flush=True)
 
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -198,7 +236,7 @@ def main():
     gu_tf = gemm_flops["gate_up_gemm"] / (gu_us * 1e-6) / 1e12
     roofline = {"kernel": "nvfp4 grouped GEMM gate_up (grouped_gemm_kernel)", "bound": "mfma",
                 "achieved": round(gu_tf, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gu_tf / PEAK_F16_TFLOPS, 4), "traffic": None,
+                "frac": round(gu_tf / PEAK_F16_TFLOPS, 4), "traffic": measured_traffic(),
                 "work_per_launch": f"{gemm_flops['gate_up_gemm']:.4e} FLOP (2 * {Rr} rows * 2048 * 1536)",
                 "avg_launch_us": round(gu_us, 2)}
 
