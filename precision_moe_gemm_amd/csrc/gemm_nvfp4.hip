@@ -14,24 +14,26 @@
 // block-scaled FP4 MFMA takes one power-of-two scale per 32 elements and
 // cannot carry an E4M3 scale per 16 elements exactly.)
 //
-// Structure.  Two independent 256-thread workgroups share each CU (about 77
-// KiB of LDS each), so one workgroup's barriers, decode and epilogue stores
-// run while the other keeps the matrix cores busy.  Workgroup tile 128 x 256
-// (rows of one expert x output columns), K-step 64; wavefront w owns the
-// columns [64w, 64w+64) for all 128 rows as 4 x 2 MFMA 32x32x16 tiles.  The
-// MFMA computes C^T tiles (weights as its first operand), which leaves 4
-// consecutive output columns in each lane for 16-byte stores.
+// Structure.  One 512-thread workgroup per CU (about 140 KiB of LDS), two
+// wavefronts per SIMD.  Workgroup tile 128 x 512 (rows of one expert x output
+// columns), K-step 64; wavefront w owns the columns [64w, 64w+64) for all 128
+// rows as 4 x 2 MFMA 32x32x16 tiles.  The MFMA computes C^T tiles (weights as
+// its first operand), which leaves 4 consecutive output columns in each lane
+// for 16-byte stores.
 //   * FP4 codes (32 B per row per K-step) and E4M3 scales (4 B per row) of
 //     both operands go from global memory straight into LDS
 //     (global_load_lds) in a 3-stage ring: the loads of K-step g+3 are issued
 //     when K-step g starts, two full K-steps before they are read.
-//   * The activation tile is shared by the 4 wavefronts, so it is decoded once
+//   * The activation tile is shared by the 8 wavefronts, so it is decoded once
 //     per K-step, cooperatively, into an FP16 tile in LDS (128 B rows, 16-byte
 //     chunks XOR-swizzled by row); each wavefront decodes only its own weight
 //     fragments, in registers.  Both decodes of K-step g+1 are interleaved with
 //     the MFMAs of K-step g, so one barrier per K-step suffices.
 //   * Decoding is v_cvt_scalef32_pk_f16_fp4 plus one packed FP16 multiply by
 //     the block scale per element pair.
+//   * A tile's epilogue runs after the first barrier of the next tile: its
+//     output stores are then younger than every load that a later K-step
+//     waits for, so no wait has to cover them.
 // Lane half h (lanes 32h..32h+31) of every MFMA takes the elements
 // [32h, 32h+32) of the K-step, i.e. block scales 2h and 2h+1, and feeds 8 of
 // them to each of the 4 MFMA K-slices.  Both operands use the same
@@ -50,14 +52,21 @@
 namespace nvfp4moe {
 namespace g5 {
 
-constexpr int BM = 128, BN = 256, BK = 64;
+constexpr int BM = 128, BN = 512, BK = 64;
 constexpr int kStages = 3;
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowB = BK / 2;                // 32 code bytes per row per K-step
 constexpr int kScB = BK / 16;                // 4 scale bytes per row per K-step
 constexpr int WN = BN / kWaves;              // 64 columns per wavefront
 constexpr int FA = BM / 32, FB = WN / 32;    // 4 x 2 MFMA 32x32 tiles per wavefront
+// Load instructions per K-step (one wavefront instruction fills 1 KiB of LDS):
+// codes of 32 rows each (activation rows first, then weight rows), and block
+// scales (or, once per tile, row scales) of 64 rows each.
+constexpr int kCI = (BM + BN) * kRowB / 1024;     // 20 code instructions
+constexpr int kSI = (BM + BN) / 64;               // 10 scale instructions
+constexpr int kCIW = (kCI + kWaves - 1) / kWaves; // per wavefront, at most
+constexpr int kSIW = (kSI + kWaves - 1) / kWaves;
 constexpr int kA16Row = BK * 2;              // 128 B per row of the decoded activation tile
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that the range check drops
 
@@ -69,17 +78,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 struct __align__(16) Stage {
   uint8_t a[BM * kRowB];       // 4 KiB FP4 activation codes, row-major
-  uint8_t w[BN * kRowB];       // 8 KiB FP4 weight codes, row-major
+  uint8_t w[BN * kRowB];       // 16 KiB FP4 weight codes, row-major (directly after a)
   uint8_t as[BM * kScB];       // 512 B
-  uint8_t ws[BN * kScB];       // 1 KiB (directly after as)
+  uint8_t ws[BN * kScB];       // 2 KiB (directly after as)
 };
 
 struct __align__(16) Smem {
   Stage st[kStages];
   uint8_t a16[2][BM * kA16Row];   // 2 x 16 KiB decoded activations (FP16)
-  float rs_a[BM];                 // row scales of the tile's rows (epilogue)
-  float rs_w[BN];                 // row scales of the tile's weight rows (directly after rs_a)
-  uint16_t tile_start[NVFP4MOE_MAX_EXPERTS + 1];   // m-tiles before expert e
+  uint8_t stg[kWaves][4096];      // per-wavefront staging of one 32 x 32 FP32 output tile
+  float rs[2][BM + BN];            // row scales of a tile's rows, then of its weight rows (epilogue)
+  int tile_start[NVFP4MOE_MAX_EXPERTS + 1];   // m-tiles before expert e
 };
 
 // byte offset of 16-byte chunk c (0..7) of row r in the FP16 activation tile
@@ -135,9 +144,10 @@ __device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t voff, con
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ void wait_vmcnt(int n) {
-  // s_waitcnt with expcnt and lgkmcnt at their maxima: vmcnt(n), n in {0, 4, 5}
+  // s_waitcnt with expcnt and lgkmcnt at their maxima: vmcnt(n), n in {0, 3, 4, 5}
   if (n == 5) __builtin_amdgcn_s_waitcnt(0x0F75);
   else if (n == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
+  else if (n == 3) __builtin_amdgcn_s_waitcnt(0x0F73);
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
@@ -146,13 +156,13 @@ struct Tile {
   int e, m0, rows, n0;
 };
 
-__device__ __forceinline__ Tile tile_at(int L, int n_tiles, const uint16_t* tile_start, int E,
+__device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_start, int E,
                                         const int32_t* __restrict__ offsets) {
   const int tm = L / n_tiles, tn = L - tm * n_tiles;
   int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if ((int)tile_start[mid] <= tm) lo = mid; else hi = mid;
+    if (tile_start[mid] <= tm) lo = mid; else hi = mid;
   }
   // the values are the same in every lane: keep them in scalar registers
   Tile t;
@@ -187,16 +197,18 @@ void grouped_gemm_kernel(
         const int y = __shfl_up(incl, off, kWave);
         if (lane >= off) incl += y;
       }
-      if (e < E) sm.tile_start[e] = (uint16_t)(carry + incl - v);
+      if (e < E) sm.tile_start[e] = carry + incl - v;
       carry += __shfl(incl, kWave - 1, kWave);
     }
-    if (lane == 0) sm.tile_start[E] = (uint16_t)carry;
+    if (lane == 0) sm.tile_start[E] = carry;
   }
   __syncthreads();
 
   const int n_tiles = (N + BN - 1) / BN;
-  const int total = __builtin_amdgcn_readfirstlane((int)sm.tile_start[E]) * n_tiles;
+  const int total = __builtin_amdgcn_readfirstlane(sm.tile_start[E]) * n_tiles;
   // XCD-contiguous tile ranges when the grid is a multiple of 8 workgroups
+  // (workgroups go to the XCDs round-robin); the range's workgroups take its
+  // tiles in turn
   int begin, end, step;
   if ((gridDim.x & 7) == 0) {
     const int per = (total + 7) / 8;
@@ -213,7 +225,8 @@ void grouped_gemm_kernel(
 
   const uint32_t kb = (uint32_t)K / 2, ks = (uint32_t)K / 16;
   const int nk = K / BK;
-  const int n_scale_loads = wave < 2 ? 2 : 1;   // 6 scale-load instructions over 4 wavefronts
+  // instructions q = wave + kWaves * u of each kind fall to this wavefront
+  const int n_loads = (kCI - wave + kWaves - 1) / kWaves + (kSI - wave + kWaves - 1) / kWaves;
 
   // ---------------------------------------------------------------- loads
   // Load cursor: the next K-step to load is (ltile, lk).  Each lane's sources
@@ -221,7 +234,7 @@ void grouped_gemm_kernel(
   // operand under 4 GiB).  A wavefront instruction fills 1 KiB of LDS: 32 code
   // rows (lane l -> row l/2, 16-byte half l%2) or 64 scale dwords.
   int lL = begin, lk = 0;
-  uint32_t off_a, off_w[2], off_s[2];
+  uint32_t off_c[kCIW], off_s[kSIW];
   // Weight K-step strides: row-major [E][N][K/2] moves 32 code bytes (4 scale
   // bytes) along a row per K-step; the K-tiled layout [E][K/64][N][32] moves
   // one whole slab of N rows, and a slab of 32 consecutive rows is 1 KiB of
@@ -232,16 +245,20 @@ void grouped_gemm_kernel(
     const Tile t = tile_at(L, n_tiles, sm.tile_start, E, offsets);
     const int m_last = t.m0 + t.rows - 1;
     const int half = lane & 1;
-    off_a = (uint32_t)min(t.m0 + 32 * wave + (lane >> 1), m_last) * kb + half * 16;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t n = (uint32_t)min(t.n0 + 64 * wave + 32 * u + (lane >> 1), N - 1);
-      off_w[u] = w_tiled ? ((uint32_t)t.e * nk * N + n) * kRowB + half * 16
-                         : ((uint32_t)t.e * N + n) * kb + half * 16;
+    for (int u = 0; u < kCIW; ++u) {
+      const int q = wave + kWaves * u;   // code instruction: 0..3 -> A rows, 4.. -> W rows
+      if (q < BM / 32) {
+        off_c[u] = (uint32_t)min(t.m0 + 32 * q + (lane >> 1), m_last) * kb + half * 16;
+      } else {
+        const uint32_t n = (uint32_t)min(t.n0 + 32 * (q - BM / 32) + (lane >> 1), N - 1);
+        off_c[u] = w_tiled ? ((uint32_t)t.e * nk * N + n) * kRowB + half * 16
+                           : ((uint32_t)t.e * N + n) * kb + half * 16;
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int q = wave + 4 * u;        // scale instruction: 0,1 -> A rows, 2..5 -> W rows
+    for (int u = 0; u < kSIW; ++u) {
+      const int q = wave + kWaves * u;   // scale instruction: 0,1 -> A rows, 2.. -> W rows
       if (q < 2) {
         off_s[u] = (uint32_t)min(t.m0 + 64 * q + lane, m_last) * ks;
       } else {
@@ -256,39 +273,40 @@ void grouped_gemm_kernel(
     if (lL >= end) return 0;
     const uint32_t ka = (uint32_t)lk * kRowB, kss = (uint32_t)lk * kScB;
     const uint32_t kw = (uint32_t)lk * wstep_c, kws = (uint32_t)lk * wstep_s;
-    lds_dma16(a_codes, ka + off_a, S.a + wave * 1024);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) lds_dma16(w_codes, kw + off_w[u], S.w + (2 * wave + u) * 1024);
+    for (int u = 0; u < kCIW; ++u) {
+      const int q = wave + kWaves * u;
+      if (q < BM / 32) lds_dma16(a_codes, ka + off_c[u], S.a + q * 1024);
+      else if (q < kCI) lds_dma16(w_codes, kw + off_c[u], S.a + q * 1024);
+    }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int q = wave + 4 * u;
+    for (int u = 0; u < kSIW; ++u) {
+      const int q = wave + kWaves * u;
       if (q < 2) lds_dma4(a_bscales, kss + off_s[u], S.as + q * 256);
-      else if (q < 6) lds_dma4(w_bscales, kws + off_s[u], S.as + q * 256);
+      else if (q < kSI) lds_dma4(w_bscales, kws + off_s[u], S.as + q * 256);
     }
     if (++lk == nk) {
       lk = 0;
       lL += step;
       if (lL < end) set_load_tile(lL);
     }
-    return 3 + n_scale_loads;
+    return n_loads;
   };
 
   // ---------------------------------------------------------------- decodes
-  // activation decode: thread -> row tid/2, elements [32 (tid%2), +32)
-  const int drow = tid >> 1, dhalf = tid & 1;
-  uint4 da;          // raw codes of the next K-step's activation share
-  uint32_t dsc;      // its two block scales
+  // activation decode: thread -> row tid/4, elements [16 (tid%4), +16), i.e.
+  // one scale block and 16-byte chunks 2 (tid%4), +1 of the FP16 row
+  const int drow = tid >> 2, dq = tid & 3;
+  uint2 da;          // raw codes of the next K-step's activation share
+  uint32_t dsc;      // its block scale
   auto read_a = [&](const Stage& S) __attribute__((always_inline)) {
-    da = *reinterpret_cast<const uint4*>(S.a + drow * kRowB + dhalf * 16);
-    dsc = *reinterpret_cast<const uint16_t*>(S.as + drow * kScB + dhalf * 2);
+    da = *reinterpret_cast<const uint2*>(S.a + drow * kRowB + dq * 8);
+    dsc = S.as[drow * kScB + dq];
   };
   auto decode_a = [&](uint8_t* A16) __attribute__((always_inline)) {
-    const uint32_t s0 = scale_pair(dsc & 0xFF), s1 = scale_pair(dsc >> 8);
-    const int c0 = 4 * dhalf;
-    *reinterpret_cast<half8*>(A16 + a16_off(drow, c0 + 0)) = decode8(da.x, s0);
-    *reinterpret_cast<half8*>(A16 + a16_off(drow, c0 + 1)) = decode8(da.y, s0);
-    *reinterpret_cast<half8*>(A16 + a16_off(drow, c0 + 2)) = decode8(da.z, s1);
-    *reinterpret_cast<half8*>(A16 + a16_off(drow, c0 + 3)) = decode8(da.w, s1);
+    const uint32_t s0 = scale_pair(dsc);
+    *reinterpret_cast<half8*>(A16 + a16_off(drow, 2 * dq + 0)) = decode8(da.x, s0);
+    *reinterpret_cast<half8*>(A16 + a16_off(drow, 2 * dq + 1)) = decode8(da.y, s0);
   };
   // weight fragments: fragment f of this wavefront = W rows 64 wave + 32 f +
   // (lane % 32); the lane's 32 elements [32h, 32h+32) of the K-step are 16
@@ -376,69 +394,50 @@ void grouped_gemm_kernel(
     }
   };
 
-  // The K-steps of one tile.  At the top of each: the loads of the next
-  // K-step have landed (those of the one after may still be in flight, unless
-  // epilogue stores are pending, whose completion order against loads is not
-  // guaranteed); the barrier publishes them and the decoded activations of
-  // this K-step, and frees the stage that the new loads go to.
-  // Row scales of a tile for its epilogue, into LDS (issued at the top of the
-  // tile's last K-step, ahead of that step's loads, so that waiting for the
-  // loads counted in n_last also waits for these)
-  auto issue_rscales = [&](const Tile& t) __attribute__((always_inline)) {
+  // Row scales of a tile for its epilogue, into one of two LDS buffers (tile
+  // parity): issued at the top of the tile's last K-step, ahead of that step's
+  // loads, so that waiting for the loads counted in n_last also waits for them.
+  auto issue_rscales = [&](const Tile& t, int rb) __attribute__((always_inline)) {
+    const uint8_t* dst = reinterpret_cast<const uint8_t*>(sm.rs[rb]);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int q = wave + 4 * u;        // 0,1 -> A rows, 2..5 -> W rows
+    for (int u = 0; u < kSIW; ++u) {
+      const int q = wave + kWaves * u;   // 0,1 -> A rows, 2.. -> W rows
       if (q < 2)
         lds_dma4(reinterpret_cast<const uint8_t*>(a_rscales),
-                 (uint32_t)min(t.m0 + 64 * q + lane, t.m0 + t.rows - 1) * 4u,
-                 reinterpret_cast<const uint8_t*>(sm.rs_a) + q * 256);
-      else if (q < 6)
+                 (uint32_t)min(t.m0 + 64 * q + lane, t.m0 + t.rows - 1) * 4u, dst + q * 256);
+      else if (q < kSI)
         lds_dma4(reinterpret_cast<const uint8_t*>(w_rscales),
-                 ((uint32_t)t.e * N + min(t.n0 + 64 * (q - 2) + lane, N - 1)) * 4u,
-                 reinterpret_cast<const uint8_t*>(sm.rs_a) + q * 256);
+                 ((uint32_t)t.e * N + min(t.n0 + 64 * (q - 2) + lane, N - 1)) * 4u, dst + q * 256);
     }
   };
 
-  auto run_tile = [&](auto full_tag, int fa_eff, bool after_stores, const Tile& t) __attribute__((always_inline)) {
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_vmcnt(kt == 0 && after_stores ? 0 : n_last);
-      lds_barrier();
-      if (kt == nk - 1) issue_rscales(t);
-      n_last = issue_loads(sm.st[sc]);
-      mma_step(full_tag, fa_eff);
-      sc = sc == kStages - 1 ? 0 : sc + 1;
-      ab ^= 1;
-    }
-  };
-
-  for (int L = begin; L < end; L += step) {
-    const Tile t = tile_at(L, n_tiles, sm.tile_start, E, offsets);
-    const int fa_eff = (t.rows + 31) >> 5;
-    if (fa_eff == FA) run_tile(std::true_type{}, FA, L != begin, t);
-    else run_tile(std::false_type{}, fa_eff, L != begin, t);
-
-    // epilogue: C = (acc * s_A[row]) * s_W[col].  Tile (i, j) of the lane
-    // holds row 32i + lane%32, columns 32j + 8q + 4h .. +3 (q = 0..3).  Each
-    // 32 x 32 tile goes through a 4 KiB slice of the activation buffer that the
-    // last K-step read (16-byte chunks XOR-swizzled by row) and leaves as four
-    // stores of 8 rows x 128 contiguous bytes: whole cache lines.  Rows past
-    // the tile's valid rows fall outside the buffer's range and are dropped by
-    // the hardware; columns past N get an out-of-range offset.
-    wait_vmcnt(n_last);    // this wavefront's row-scale loads have landed
-    lds_barrier();         // everyone's, and nobody reads a16[ab ^ 1] any more
+  // epilogue: C = (acc * s_A[row]) * s_W[col].  Tile (i, j) of the lane holds
+  // row 32i + lane%32, columns 32j + 8q + 4h .. +3 (q = 0..3).  Each 32 x 32
+  // tile goes through the wavefront's 4 KiB staging slice (16-byte chunks
+  // XOR-swizzled by row) and leaves as four stores of 8 rows x 128 contiguous
+  // bytes: whole cache lines.  Rows past the tile's valid rows fall outside the
+  // buffer's range and are dropped by the hardware; columns past N get an
+  // out-of-range offset.  The accumulators are cleared for the next tile.
+  auto epilogue = [&](const Tile& t, int rb) __attribute__((always_inline)) {
+    const float* rs_a = sm.rs[rb];
+    const float* rs_w = sm.rs[rb] + BM;
     float sa[FA];
 #pragma unroll
-    for (int i = 0; i < FA; ++i) sa[i] = sm.rs_a[32 * i + l32];
-    uint8_t* stg = sm.a16[ab ^ 1] + wave * 4096;
+    for (int i = 0; i < FA; ++i) sa[i] = rs_a[32 * i + l32];
+    uint8_t* stg = sm.stg[wave];
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         c + (int64_t)t.m0 * N, (short)0, t.rows * N * 4, 0x00020000);
     const int srow = lane >> 3, sch = lane & 7;   // store layout: 8 rows x 8 chunks per instruction
+    // the lane's row offset, recomputed per tile: kept opaque so that the
+    // compiler does not hoist sixteen per-lane row offsets out of the tile loop
+    uint32_t srowN = (uint32_t)(srow * N);
+    asm volatile("" : "+v"(srowN));
 #pragma unroll
     for (int j = 0; j < FB; ++j) {
       float4 swv[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        swv[q] = *reinterpret_cast<const float4*>(&sm.rs_w[WN * wave + 32 * j + 8 * q + 4 * h]);
+        swv[q] = *reinterpret_cast<const float4*>(&rs_w[WN * wave + 32 * j + 8 * q + 4 * h]);
       const int n = t.n0 + WN * wave + 32 * j + 4 * sch;
 #pragma unroll
       for (int i = 0; i < FA; ++i) {
@@ -455,13 +454,56 @@ void grouped_gemm_kernel(
         for (int r = 0; r < 4; ++r) {
           const int row = 8 * r + srow;
           const float4 v = *reinterpret_cast<const float4*>(stg + row * 128 + ((sch ^ (row & 7)) << 4));
-          const uint32_t off = n < N ? (uint32_t)((32 * i + row) * N + n) * 4u : kOutOfRange;
+          const uint32_t off = n < N ? ((uint32_t)((32 * i + 8 * r) * N) + srowN + (uint32_t)n) * 4u : kOutOfRange;
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsrc, off, 0, 0);
         }
         acc[i][j] = floatx16{};
       }
     }
+  };
+
+  // The K-steps of one tile.  At the top of each: this wavefront's loads of
+  // the next K-step have landed (those of the one after may still be in
+  // flight); the barrier publishes everyone's, and the decoded activations of
+  // this K-step, and frees the stage that the new loads go to.  The previous
+  // tile's epilogue runs after the first of these barriers, so that its stores
+  // are issued after every load that this wait has to see complete (vmcnt
+  // cannot single out loads that are older than pending stores); its row
+  // scales landed with the loads it waited for, and the tile's own row scales
+  // go to the other buffer.
+  int rbuf = 0;
+  auto run_tile = [&](auto full_tag, int fa_eff, const Tile& t) __attribute__((always_inline)) {
+    mma_step(full_tag, fa_eff);   // K-step 0: its wait, barrier and loads are done by the caller
+    sc = sc == kStages - 1 ? 0 : sc + 1;
+    ab ^= 1;
+    for (int kt = 1; kt < nk; ++kt) {
+      wait_vmcnt(n_last);
+      lds_barrier();
+      if (kt == nk - 1) issue_rscales(t, rbuf);
+      n_last = issue_loads(sm.st[sc]);
+      mma_step(full_tag, fa_eff);
+      sc = sc == kStages - 1 ? 0 : sc + 1;
+      ab ^= 1;
+    }
+  };
+
+  Tile prev{0, 0, 0, 0};
+  for (int L = begin; L < end; L += step) {
+    const Tile t = tile_at(L, n_tiles, sm.tile_start, E, offsets);
+    const int fa_eff = (t.rows + 31) >> 5;
+    wait_vmcnt(n_last);
+    lds_barrier();
+    epilogue(prev, rbuf ^ 1);   // before the first tile: no rows, every store is dropped
+    if (nk == 1) issue_rscales(t, rbuf);
+    n_last = issue_loads(sm.st[sc]);
+    if (fa_eff == FA) run_tile(std::true_type{}, FA, t);
+    else run_tile(std::false_type{}, fa_eff, t);
+    prev = t;
+    rbuf ^= 1;
   }
+  wait_vmcnt(0);    // the last tile's row scales (no loads are left)
+  lds_barrier();
+  epilogue(prev, rbuf ^ 1);
 }
 
 }  // namespace g5
@@ -494,8 +536,8 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uin
   const int64_t n_tiles = (N + g5::BN - 1) / g5::BN;
   const int64_t max_tiles = ((R_cap + g5::BM - 1) / g5::BM + E) * n_tiles;
   if (max_tiles > INT32_MAX) return NVFP4_ERR_SHAPE;
-  // persistent grid: two workgroups per CU on a 256-CU device, a multiple of 8
-  int64_t grid = max_tiles < 512 ? max_tiles : 512;
+  // persistent grid: one workgroup per CU on a 256-CU device, a multiple of 8
+  int64_t grid = max_tiles < 256 ? max_tiles : 256;
   if (grid >= 8) grid &= ~7ll;
   hipStream_t s = static_cast<hipStream_t>(stream);
   g5::grouped_gemm_kernel<<<(unsigned)grid, g5::kThreads, 0, s>>>(
