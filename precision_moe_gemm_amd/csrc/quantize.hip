@@ -403,105 +403,70 @@ __global__ __launch_bounds__(256) void quantize_route_kernel(
 
 // Route + permute + quantise in two launches.
 //
-// The plan: one workgroup reads the whole routing list once and counts it per
-// (4096-entry chunk, expert) in LDS, then writes
-//   base[c][e] = offsets[e] + (entries of e in chunks before c)
-// and the expert offsets.  One workgroup keeps every count on chip: no
-// global round trips between the steps.  Used while nchunks * E <= kPlanLds.
+// The count: one 1024-thread workgroup per chunk of 4096 routing entries
+// counts the chunk's entries per expert in LDS and writes the counts,
+// cnt[c][e].  Workgroups are independent, so the pass costs one load round
+// trip.  Used while nchunks * E <= kCountTable (the main pass reads the whole
+// table in every workgroup).
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanChunkLog = 12;        // 4096 routing entries per plan chunk
-constexpr int kPlanLds = 16384;          // ints of LDS for the (chunk, expert) counts
+constexpr int kPlanChunkLog = 12;        // 4096 routing entries per chunk
+constexpr int kCountTable = 4096;        // ints of (chunk, expert) counts the main pass reads
 
 inline int plan_chunks(int64_t n) { return n > 0 ? (int)((n + (1 << kPlanChunkLog) - 1) >> kPlanChunkLog) : 1; }
 
-__global__ __launch_bounds__(kPlanThreads) void route_plan1_kernel(
-    const int32_t* __restrict__ ids, int n, int E, int nchunks, int32_t* __restrict__ base,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ dev_err) {
-  __shared__ int32_t cnt[kPlanLds];
-  __shared__ int32_t tot[NVFP4MOE_MAX_EXPERTS];
-  __shared__ int32_t wsum[kPlanThreads / kWave];
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  for (int i = tid; i < nchunks * E; i += kPlanThreads) cnt[i] = 0;
+__global__ __launch_bounds__(kPlanThreads) void route_count_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int32_t* __restrict__ cnt_out,
+    int32_t* __restrict__ dev_err) {
+  __shared__ int32_t cnt[NVFP4MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kPlanThreads) cnt[e] = 0;
   __syncthreads();
+  const int i0 = (blockIdx.x << kPlanChunkLog) + 4 * tid;   // 4 entries per thread
+  int v[4];
+  if (i0 + 3 < n && (reinterpret_cast<uintptr_t>(ids) & 15) == 0) {
+    const int4 q = *reinterpret_cast<const int4*>(ids + i0);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = i0 + u < n ? ids[i0 + u] : 0;
+  }
   bool bad = false;
-  const bool vec = (reinterpret_cast<uintptr_t>(ids) & 15) == 0;
-  for (int i0 = 4 * tid; i0 < n; i0 += 4 * kPlanThreads * 4) {
-    int4 q[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 4 * kPlanThreads;
-      if (vec && i + 3 < n) {
-        q[u] = *reinterpret_cast<const int4*>(ids + i);
-      } else {
-        q[u].x = i < n ? ids[i] : -1;
-        q[u].y = i + 1 < n ? ids[i + 1] : -1;
-        q[u].z = i + 2 < n ? ids[i + 2] : -1;
-        q[u].w = i + 3 < n ? ids[i + 3] : -1;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * 4 * kPlanThreads;
-      const int v[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (i + c >= n) continue;
-        const int e = v[c];
-        if (e >= 0 && e < E) atomicAdd(&cnt[((i + c) >> kPlanChunkLog) * E + e], 1);
-        else bad = true;
-      }
-    }
+  for (int u = 0; u < 4; ++u) {
+    if (i0 + u >= n) continue;
+    if (v[u] >= 0 && v[u] < E) atomicAdd(&cnt[v[u]], 1);
+    else bad = true;
   }
   if (bad && dev_err) atomicOr(dev_err, NVFP4_DEVERR_BAD_EXPERT);
   __syncthreads();
-  // per expert: exclusive prefix over chunks, in place, and the total
-  for (int e = tid; e < E; e += kPlanThreads) {
-    int acc = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int v = cnt[c * E + e];
-      cnt[c * E + e] = acc;
-      acc += v;
-    }
-    tot[e] = acc;
-  }
-  __syncthreads();
-  // exclusive scan of the totals over experts: per wavefront, then across
-  const int v = tid < E ? tot[tid] : 0;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += y;
-  }
-  if (lane == kWave - 1) wsum[wave] = incl;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  if (tid < E) tot[tid] = before + incl - v;
-  if (tid == kPlanThreads - 1) offsets[E] = before + incl;
-  __syncthreads();
-  for (int e = tid; e < E; e += kPlanThreads) offsets[e] = tot[e];
-  for (int i = tid; i < nchunks * E; i += kPlanThreads) base[i] = cnt[i] + tot[i % E];
+  for (int e = tid; e < E; e += kPlanThreads) cnt_out[blockIdx.x * E + e] = cnt[e];
 }
 
 // The main pass.  Workgroup w (8 wavefronts) owns tokens [8w, 8w + 8), one
-// per wavefront.  Its activations and every routing id it needs (its own
-// entries, and its chunk's entries before them, at most 4095) are loaded at
-// the start.  It counts per expert the chunk's entries before its first one,
-// ranks its own entries in (token, slot) order by ballot matching, and turns
-// (chunk, expert, rank) into rows with the plan's bases.  Each token is
-// quantised once and written to its k rows.
+// per wavefront.  Its activations, the count table and every routing id it
+// needs (its own entries, and its chunk's entries before them, at most 4095)
+// are loaded at the start.  From the table it forms the expert offsets and
+// the first row of each expert in its chunk(s); it counts per expert the
+// chunk's entries before its first one, ranks its own entries in (token, slot)
+// order by ballot matching, and so places every entry.  Each token is
+// quantised once and written to its k rows.  Workgroup 0 also writes the
+// expert offsets.
 constexpr int kQpWaves = 8;
 constexpr int kQpThreads = kQpWaves * 64;
 constexpr int kQpPre = (1 << kPlanChunkLog) / kQpThreads;   // prefix ids per thread (8)
+constexpr int kQpExp = NVFP4MOE_MAX_EXPERTS / kQpThreads;   // experts per thread (2)
 
 template <int NCH>
 __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
     const uint16_t* __restrict__ x, int64_t T, int K, const int32_t* __restrict__ ids, int k, int E,
-    const int32_t* __restrict__ base, uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales,
-    float* __restrict__ rscales, int32_t* __restrict__ row_to_tk, int32_t* __restrict__ tk_to_row) {
-  __shared__ int32_t pre[2][NVFP4MOE_MAX_EXPERTS];
+    const int32_t* __restrict__ cnt, int nchunks, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ bscales, float* __restrict__ rscales, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_to_tk, int32_t* __restrict__ tk_to_row) {
+  __shared__ int32_t pre[2][NVFP4MOE_MAX_EXPERTS];     // chunk entries before e0, per part
+  __shared__ int32_t sbase[2][NVFP4MOE_MAX_EXPERTS];   // first row of expert e in part's chunk
+  __shared__ int32_t wsum[kQpWaves];
   __shared__ int32_t rows[kQpWaves * NVFP4MOE_MAX_TOPK];
+  __shared__ int32_t tab[kCountTable];                  // the count table
   const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int64_t t = (int64_t)blockIdx.x * kQpWaves + wave;
   const int n = (int)(T * k);
@@ -509,9 +474,16 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
   const int e1 = min(e0 + kQpWaves * k, n);                        // one past the last
   const int cs = (e0 >> kPlanChunkLog) << kPlanChunkLog;          // start of e0's chunk
   const int second = cs + (1 << kPlanChunkLog);                    // start of the next chunk
+  const int c0 = e0 >> kPlanChunkLog;                              // e0's chunk
 
   uint4 raw[NCH];
   if (t < T) load_bf16_raw<NCH>(x + t * (int64_t)K, K, raw);
+  // the count table, into LDS (independent loads, all in flight together)
+#pragma unroll
+  for (int u = 0; u < kCountTable / kQpThreads; ++u) {
+    const int i = u * kQpThreads + tid;
+    if (i < nchunks * E) tab[i] = cnt[i];
+  }
   // the chunk's ids before e0 (strided over the workgroup) and, in wavefront
   // 0, the group's own ids
   int pv[kQpPre];
@@ -529,6 +501,47 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
 
   for (int e = tid; e < E; e += kQpThreads) { pre[0][e] = 0; pre[1][e] = 0; }
   __syncthreads();
+  // per expert (thread tid owns experts 2 tid, 2 tid + 1): the total, and the
+  // entries in the chunks before c0 and before c0 + 1
+  int tot[kQpExp], b0[kQpExp], b1[kQpExp];
+#pragma unroll
+  for (int u = 0; u < kQpExp; ++u) { tot[u] = 0; b0[u] = 0; b1[u] = 0; }
+  for (int c = 0; c < nchunks; ++c) {
+#pragma unroll
+    for (int u = 0; u < kQpExp; ++u) {
+      const int e = kQpExp * tid + u;
+      const int v = e < E ? tab[c * E + e] : 0;
+      tot[u] += v;
+      if (c < c0) b0[u] += v;
+      if (c <= c0) b1[u] += v;
+    }
+  }
+  // expert offsets: exclusive scan of the totals over experts
+  int mine = 0;
+#pragma unroll
+  for (int u = 0; u < kQpExp; ++u) mine += tot[u];
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  int off_e = before + incl - mine;   // offset of expert kQpExp * tid
+#pragma unroll
+  for (int u = 0; u < kQpExp; ++u) {
+    const int e = kQpExp * tid + u;
+    if (e < E) {
+      sbase[0][e] = off_e + b0[u];
+      sbase[1][e] = off_e + b1[u];
+      if (blockIdx.x == 0) offsets[e] = off_e;
+    }
+    off_e += tot[u];
+  }
+  if (blockIdx.x == 0 && tid == kQpThreads - 1) offsets[E] = before + incl;
 #pragma unroll
   for (int u = 0; u < kQpPre; ++u) {
     const int e = pv[u];
@@ -557,9 +570,9 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
       const int r = __popcll(peers & lt_mask);
       int row = -1;
       if (valid) {
-        const int before = pre[part][e];
-        row = base[(idx >> kPlanChunkLog) * E + e] + before + r;
-        if (r == 0) pre[part][e] = before + __popcll(peers);
+        const int bef = pre[part][e];
+        row = sbase[part][e] + bef + r;
+        if (r == 0) pre[part][e] = bef + __popcll(peers);
       }
       if (idx < e1) {
         tk_to_row[idx] = row;
@@ -738,22 +751,20 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
   unsigned long long* arrivals = static_cast<unsigned long long*>(workspace);
   int32_t* table = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + kPlanArrivalBytes);
   const int pchunks = plan_chunks(n);
-  if ((int64_t)pchunks * E <= kPlanLds && n <= INT32_MAX / 2 && H <= 4096) {
-    // plan in one workgroup, then rank + quantise + scatter
-    route_plan1_kernel<<<1, kPlanThreads, 0, s>>>(topk_ids, (int)n, E, pchunks, table,
-                                                  expert_offsets, dev_err);
-    if (T > 0) {
-      const unsigned grid = (unsigned)((T + kQpWaves - 1) / kQpWaves);
-      switch (nch_for(H)) {
-#define QP_LAUNCH(C)                                                                           \
-        case C:                                                                                \
-          quantize_permute_kernel<C><<<grid, kQpThreads, 0, s>>>(x, T, (int)H, topk_ids, (int)k, \
-              (int)E, table, codes, bscales, rscales, row_to_tk, tk_to_row);                   \
-          break;
-        QP_LAUNCH(1) QP_LAUNCH(2) QP_LAUNCH(4)
-        default: QP_LAUNCH(8)
+  if (T > 0 && (int64_t)pchunks * E <= kCountTable && n <= INT32_MAX / 2 && H <= 4096) {
+    // count per (chunk, expert), then offsets + rank + quantise + scatter
+    route_count_kernel<<<pchunks, kPlanThreads, 0, s>>>(topk_ids, (int)n, E, table, dev_err);
+    const unsigned grid = (unsigned)((T + kQpWaves - 1) / kQpWaves);
+    switch (nch_for(H)) {
+#define QP_LAUNCH(C)                                                                             \
+      case C:                                                                                    \
+        quantize_permute_kernel<C><<<grid, kQpThreads, 0, s>>>(x, T, (int)H, topk_ids, (int)k,   \
+            (int)E, table, pchunks, codes, bscales, rscales, expert_offsets, row_to_tk,          \
+            tk_to_row);                                                                          \
+        break;
+      QP_LAUNCH(1) QP_LAUNCH(2) QP_LAUNCH(4)
+      default: QP_LAUNCH(8)
 #undef QP_LAUNCH
-      }
     }
   } else {
     // long routing lists or long rows: plan over chunks of 1024 entries in many

@@ -111,7 +111,10 @@ def test_quantize_permute_full_config():
                                           (1000, 128, 8, "zipf"), (777, 16, 3, "uniform"),
                                           (2049, 64, 8, "softmax"), (300, 1, 1, "uniform"),
                                           (128, 1024, 32, "uniform"),   # E > 512
-                                          (40000, 128, 8, "zipf"),      # 320k entries, one-workgroup plan
+                                          (2000, 32, 3, "zipf"),        # groups of 24 entries straddle 4096-entry chunks
+                                          (1700, 64, 5, "softmax"),     # ditto, 3 chunks
+                                          (600, 1024, 8, "uniform"),    # 2 chunks x 1024 experts in the count table
+                                          (40000, 128, 8, "zipf"),      # 320k entries: many-workgroup plan
                                           (3000, 1024, 32, "uniform")]) # 96k entries x 1024 experts: many-workgroup plan
 def test_quantize_permute_ragged(T, E, k, kind):
     x = W.activations(T, 64 if T > 10000 else 256, config=9, tensor=T)
