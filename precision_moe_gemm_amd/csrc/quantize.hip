@@ -60,8 +60,33 @@ __device__ __forceinline__ void quantize_lane_row(const float (&x)[NCH][8], RowC
     const uint32_t b = (s != 0.0f) ? e4m3_encode_nonneg(bm[c] / six_s) : 0u;
     const float d = e4m3_decode_nonneg(b) * s;
     float r[8];
+    // fl(x / d) with one division per block: y = fl(1/d), q = fl(x*y),
+    // e = x - q*d (exact, one FMA), fl(q + e*y) is the correctly rounded
+    // quotient (Markstein) while every value involved is a normal number.  With
+    // the block maximum at least 2^-80, d, 1/d and, wherever the quotient is
+    // near an E2M1 rounding tie, q and e are normal; far from the ties any
+    // small error leaves the code unchanged.  Otherwise (or for an infinity or
+    // NaN in the block) divide.  Checked against correctly rounded division on
+    // 2e7 quotients placed around every E2M1 tie.
+    bool fast = d == 0.0f || bm[c] >= 0x1p-80f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = d != 0.0f ? x[c][j] / d : x[c][j] * 0.0f;
+    for (int j = 0; j < 8; ++j) fast = fast && __builtin_isfinite(x[c][j]);
+    if (__all(fast)) {
+      const float y = 1.0f / (d != 0.0f ? d : 1.0f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float q = x[c][j] * y;
+        const float e = __builtin_fmaf(-q, d, x[c][j]);
+        const float q2 = __builtin_fmaf(e, y, q);
+        // the sign comes from x: the chain turns -0 into +0 (and a zero d
+        // gives a zero of x's sign)
+        r[j] = __builtin_copysignf(d != 0.0f ? q2 : 0.0f, x[c][j]);
+      }
+    } else {
+      const float dd = d != 0.0f ? d : 1.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = d != 0.0f ? x[c][j] / dd : x[c][j] * 0.0f;
+    }
     o.q[c] = e2m1_pack8(r);
     o.b[c] = b;
   }
@@ -476,8 +501,6 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
   const int second = cs + (1 << kPlanChunkLog);                    // start of the next chunk
   const int c0 = e0 >> kPlanChunkLog;                              // e0's chunk
 
-  uint4 raw[NCH];
-  if (t < T) load_bf16_raw<NCH>(x + t * (int64_t)K, K, raw);
   // the count table, into LDS (independent loads, all in flight together)
 #pragma unroll
   for (int u = 0; u < kCountTable / kQpThreads; ++u) {
@@ -498,6 +521,9 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
     const int idx = e0 + u * kWave + lane;
     own[u] = (wave == 0 && idx < e1) ? ids[idx] : -1;
   }
+  // the token's activations last: waiting for the ids above does not wait for them
+  uint4 raw[NCH];
+  if (t < T) load_bf16_raw<NCH>(x + t * (int64_t)K, K, raw);
 
   for (int e = tid; e < E; e += kQpThreads) { pre[0][e] = 0; pre[1][e] = 0; }
   __syncthreads();
@@ -548,6 +574,17 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
     if (e >= 0 && e < E) atomicAdd(&pre[0][e], 1);
   }
   __syncthreads();
+  // The token's codes do not depend on the routing: wavefronts 1..7 quantise
+  // while wavefront 0 ranks the group's entries, then quantises its own.
+  RowCodes<NCH> o;
+  uint32_t sw[(NCH + 7) / 8];
+  auto quantise = [&]() __attribute__((always_inline)) {
+    float v[NCH][8];
+    unpack_bf16<NCH>(raw, v);
+    quantize_lane_row<NCH>(v, o);
+    pack_scales<NCH>(o, sw);
+  };
+  if (wave != 0 && t < T) quantise();
   if (wave == 0) {
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
@@ -580,15 +617,10 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
         if (valid) row_to_tk[row] = idx;
       }
     }
+    if (t < T) quantise();
   }
   __syncthreads();
   if (t >= T) return;
-  float v[NCH][8];
-  unpack_bf16<NCH>(raw, v);
-  RowCodes<NCH> o;
-  quantize_lane_row<NCH>(v, o);
-  uint32_t sw[(NCH + 7) / 8];
-  pack_scales<NCH>(o, sw);
   const int my_row = lane < k ? rows[wave * k + lane] : -1;
   for (int slot = 0; slot < k; ++slot) {
     const int row = __shfl(my_row, slot, kWave);
