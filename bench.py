@@ -258,9 +258,45 @@ def main():
         "setup_s": round(setup_s, 1),
     }
 
+    result["practical_ceiling"] = practical_ceiling(gu_tf, per_op["quantize_permute"]["GBps"])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_bits, ids_np, wgu_bits, S, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def practical_ceiling(gate_up_tflops, qp_gbps):
+    """Rates the device sustains, measured after the timed steps (outside them):
+    FP16 MFMA issue with no memory traffic (the library's MFMA-only kernel) and a
+    512 MiB device-to-device copy; the headline kernels as fractions of these."""
+    import torch
+    import precision_moe_gemm_amd as pmg
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    iters = 20000
+    sink, flops = pmg.mfma_ceiling(iters)
+    for _ in range(3):
+        pmg.mfma_ceiling(iters, sink)
+    st.record()
+    for _ in range(5):
+        pmg.mfma_ceiling(iters, sink)
+    en.record()
+    torch.cuda.synchronize()
+    mfma_tf = 5 * flops / (st.elapsed_time(en) * 1e-3) / 1e12
+    n = 512 * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    st.record()
+    for _ in range(10):
+        b.copy_(a)
+    en.record()
+    torch.cuda.synchronize()
+    copy_gbs = 10 * 2 * n * 4 / (st.elapsed_time(en) * 1e-3) / 1e9
+    return {"mfma_f16_tflops": round(mfma_tf, 1), "copy_gbps": round(copy_gbs, 1),
+            "gate_up_frac_of_mfma": round(gate_up_tflops / mfma_tf, 4),
+            "quantize_permute_frac_of_copy": round(qp_gbps / copy_gbs, 4),
+            "how": "MFMA: 256 workgroups x 8 wavefronts of back-to-back 32x32x16 f16 MFMAs on registers; "
+                   "copy: 512 MiB device-to-device, read + write bytes"}
 
 
 def cpu_baseline(x_bits, ids, wgu_bits, S, budget_s):

@@ -240,6 +240,15 @@ NVFP4MOE_API int swiglu_backward(const float* gu, const float* dh, int64_t R_cap
                                  const float* topk_w, const int32_t* row_to_tk,
                                  uint16_t* dgu, void* stream);
 
+/* Measurement aid (no part of the MoE computation): the device's practical
+ * FP16 MFMA rate.  256 workgroups of 8 wavefronts (two per SIMD on a 256-CU
+ * MI355X) each issue `iters` rounds of 8 independent v_mfma_f32_32x32x16_f16 on
+ * register operands, then write one float per thread to sink.
+ *   iters in [1, 1e7]; sink: device, 16-byte aligned, 256 * 512 floats
+ *   FLOPs issued = 256 * 8 * iters * 8 * 32768; the caller times the stream.
+ */
+NVFP4MOE_API int nvfp4moe_mfma_ceiling(int64_t iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -62,6 +62,7 @@ SIGNATURES = {
     "permute_gather_bf16": ([_P, _I64, _I64, _I32, _P, _I32, _P, _P, _P], _c.c_int),
     "bf16_grouped_gemm": ([_P, _P, _I32, _I64, _P, _I32, _I64, _I64, _P, _P], _c.c_int),
     "swiglu_backward": ([_P, _P, _I64, _I64, _P, _I32, _P, _P, _P, _P], _c.c_int),
+    "nvfp4moe_mfma_ceiling": ([_I64, _P, _P], _c.c_int),
 }
 
 
@@ -303,3 +304,14 @@ def swiglu_backward(gu, dh, expert_offsets, topk_w=None, row_to_tk=None, dgu=Non
         _ptr(gu), _ptr(dh), R_cap, I2 // 2, _ptr(expert_offsets), E, _ptr(topk_w),
         _ptr(row_to_tk), _ptr(dgu), _stream()))
     return dgu
+
+
+def mfma_ceiling(iters: int, sink=None):
+    """Launch the FP16 MFMA-only measurement kernel on the current stream.
+
+    Returns (sink, flops issued).  Timing is the caller's."""
+    if sink is None:
+        sink = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
+    _req(sink, "sink", _F32)
+    _check("nvfp4moe_mfma_ceiling", load_library().nvfp4moe_mfma_ceiling(iters, _ptr(sink), _stream()))
+    return sink, 256 * 8 * iters * 8 * 32768

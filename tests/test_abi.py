@@ -114,6 +114,13 @@ def test_streaming_ops_host_checks(lib):
     assert lib.swiglu_backward(FAKE, FAKE, 10, 768, FAKE, 4, None, None, FAKE + 2, None) == ERR_ALIGN
 
 
+def test_mfma_ceiling_host_checks(lib):
+    assert lib.nvfp4moe_mfma_ceiling(0, None, None) == ERR_SHAPE
+    assert lib.nvfp4moe_mfma_ceiling(10_000_001, None, None) == ERR_SHAPE
+    assert lib.nvfp4moe_mfma_ceiling(10, None, None) == ERR_NULL
+    assert lib.nvfp4moe_mfma_ceiling(10, 8, None) == ERR_ALIGN
+
+
 def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(pmg, "_LIB", None)
     monkeypatch.setattr(pmg, "library_path", lambda: str(tmp_path / "missing.so"))
