@@ -216,7 +216,8 @@ NVFP4MOE_API int permute_gather_bf16(const uint16_t* x, int64_t T, int64_t H, in
  *                           used for the input gradient, contracting over out)
  *        NVFP4MOE_W_NK (1): [E][N][K]
  *   c  float [R_cap][N]
- * Requires K % 32 == 0, N % 64 == 0 (NVFP4MOE_W_KN) or N % 16 == 0 (NVFP4MOE_W_NK).
+ * Requires K % 32 == 0, N % 16 == 0, and each operand under 4 GiB (R_cap * K * 2 and
+ * E * N * K * 2 bytes).
  */
 #define NVFP4MOE_W_KN 0
 #define NVFP4MOE_W_NK 1
