@@ -69,6 +69,7 @@ constexpr int kCIW = (kCI + kWaves - 1) / kWaves; // per wavefront, at most
 constexpr int kSIW = (kSI + kWaves - 1) / kWaves;
 constexpr int kA16Row = BK * 2;              // 128 B per row of the decoded activation tile
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that the range check drops
+constexpr int kNonTemporal = 2;                 // buffer store cache policy: nt
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -455,7 +456,8 @@ void grouped_gemm_kernel(
           const int row = 8 * r + srow;
           const float4 v = *reinterpret_cast<const float4*>(stg + row * 128 + ((sch ^ (row & 7)) << 4));
           const uint32_t off = n < N ? ((uint32_t)((32 * i + 8 * r) * N) + srowN + (uint32_t)n) * 4u : kOutOfRange;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsrc, off, 0, 0);
+          // non-temporal: the output is streamed out, not kept in L2 over the tiles' operands
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsrc, off, 0, kNonTemporal);
         }
         acc[i][j] = floatx16{};
       }
