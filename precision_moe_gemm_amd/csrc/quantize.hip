@@ -211,6 +211,108 @@ __device__ __forceinline__ void load_bf16_row(const uint16_t* __restrict__ xrow,
   unpack_bf16<NCH>(raw, x);
 }
 
+// ------------------------------------------------------------------ contiguous-lane rows
+// Rows of K = 1024 * BPL elements (BPL = 1, 2, 4): lane l holds elements
+// [16 BPL l, 16 BPL (l + 1)), i.e. BPL whole scale blocks, so a block's maximum
+// needs no shuffle and a lane's codes (8 BPL bytes) and block scales (BPL
+// bytes) are contiguous: a routed row leaves in one code store and one scale
+// store per lane.  Same arithmetic as quantize_lane_row.
+template <int BPL>
+struct RowCodesC {
+  uint32_t q[2 * BPL];   // packed E2M1 codes of the lane's blocks, 8 per word
+  uint32_t b[BPL];       // E4M3 code of each block
+  float s;               // row scale (same in every lane)
+};
+
+template <int BPL>
+__device__ __forceinline__ void load_bf16_c(const uint16_t* __restrict__ xrow, uint4 (&raw)[2 * BPL]) {
+  const uint4* p = reinterpret_cast<const uint4*>(xrow + 16 * BPL * lane_id());
+#pragma unroll
+  for (int u = 0; u < 2 * BPL; ++u) raw[u] = p[u];
+}
+
+// codes of the 16 elements of one block: fl(x / d) by the quotient rules of
+// quantize_lane_row (one division per block where the values allow it)
+__device__ __forceinline__ void block_codes16(const float* x, float d, float bmax, uint32_t& w0,
+                                              uint32_t& w1) {
+  float r[16];
+  bool fast = d == 0.0f || bmax >= 0x1p-80f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) fast = fast && __builtin_isfinite(x[j]);
+  if (__all(fast)) {
+    const float y = 1.0f / (d != 0.0f ? d : 1.0f);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float q = x[j] * y;
+      const float e = __builtin_fmaf(-q, d, x[j]);
+      const float q2 = __builtin_fmaf(e, y, q);
+      r[j] = __builtin_copysignf(d != 0.0f ? q2 : 0.0f, x[j]);
+    }
+  } else {
+    const float dd = d != 0.0f ? d : 1.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r[j] = d != 0.0f ? x[j] / dd : x[j] * 0.0f;
+  }
+  w0 = e2m1_pack8(*reinterpret_cast<const float(*)[8]>(r));
+  w1 = e2m1_pack8(*reinterpret_cast<const float(*)[8]>(r + 8));
+}
+
+template <int BPL>
+__device__ __forceinline__ void quantize_lane_row_c(const uint4 (&raw)[2 * BPL], RowCodesC<BPL>& o) {
+  float x[BPL][16];
+#pragma unroll
+  for (int u = 0; u < 2 * BPL; ++u) {
+    float* v = &x[u >> 1][8 * (u & 1)];
+    v[0] = bf16_lo(raw[u].x); v[1] = bf16_hi(raw[u].x);
+    v[2] = bf16_lo(raw[u].y); v[3] = bf16_hi(raw[u].y);
+    v[4] = bf16_lo(raw[u].z); v[5] = bf16_hi(raw[u].z);
+    v[6] = bf16_lo(raw[u].w); v[7] = bf16_hi(raw[u].w);
+  }
+  float bm[BPL];
+  float am = 0.0f;
+#pragma unroll
+  for (int b = 0; b < BPL; ++b) {
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) m = fmaxf(m, __builtin_fabsf(x[b][j]));
+    bm[b] = m;
+    am = fmaxf(am, m);
+  }
+  const float a = wave_max(am);
+  const float s = a / 2688.0f;
+  const float six_s = 6.0f * s;
+  o.s = s;
+#pragma unroll
+  for (int b = 0; b < BPL; ++b) {
+    const uint32_t code = (s != 0.0f) ? e4m3_encode_nonneg(bm[b] / six_s) : 0u;
+    const float d = e4m3_decode_nonneg(code) * s;
+    block_codes16(x[b], d, bm[b], o.q[2 * b], o.q[2 * b + 1]);
+    o.b[b] = code;
+  }
+}
+
+template <int BPL>
+__device__ __forceinline__ void store_row_c(const RowCodesC<BPL>& o, int K, int64_t row,
+                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales,
+                                           float* __restrict__ rscales) {
+  const int lane = lane_id();
+  uint8_t* crow = codes + row * (int64_t)(K / 2) + 8 * BPL * lane;
+  uint8_t* brow = bscales + row * (int64_t)(K / 16) + BPL * lane;
+  if constexpr (BPL == 1) {
+    *reinterpret_cast<uint2*>(crow) = make_uint2(o.q[0], o.q[1]);
+    *brow = (uint8_t)o.b[0];
+  } else if constexpr (BPL == 2) {
+    *reinterpret_cast<uint4*>(crow) = make_uint4(o.q[0], o.q[1], o.q[2], o.q[3]);
+    *reinterpret_cast<uint16_t*>(brow) = (uint16_t)(o.b[0] | (o.b[1] << 8));
+  } else {
+    static_assert(BPL == 4, "1, 2 or 4 blocks per lane");
+    *reinterpret_cast<uint4*>(crow) = make_uint4(o.q[0], o.q[1], o.q[2], o.q[3]);
+    *reinterpret_cast<uint4*>(crow + 16) = make_uint4(o.q[4], o.q[5], o.q[6], o.q[7]);
+    *reinterpret_cast<uint32_t*>(brow) = o.b[0] | (o.b[1] << 8) | (o.b[2] << 16) | (o.b[3] << 24);
+  }
+  if (lane == 0) rscales[row] = o.s;
+}
+
 // ------------------------------------------------------------------ kernels
 template <int NCH>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(
@@ -481,7 +583,7 @@ constexpr int kQpThreads = kQpWaves * 64;
 constexpr int kQpPre = (1 << kPlanChunkLog) / kQpThreads;   // prefix ids per thread (8)
 constexpr int kQpExp = NVFP4MOE_MAX_EXPERTS / kQpThreads;   // experts per thread (2)
 
-template <int NCH>
+template <int NCH, int BPL>
 __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
     const uint16_t* __restrict__ x, int64_t T, int K, const int32_t* __restrict__ ids, int k, int E,
     const int32_t* __restrict__ cnt, int nchunks, uint8_t* __restrict__ codes,
@@ -522,8 +624,12 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
     own[u] = (wave == 0 && idx < e1) ? ids[idx] : -1;
   }
   // the token's activations last: waiting for the ids above does not wait for them
-  uint4 raw[NCH];
-  if (t < T) load_bf16_raw<NCH>(x + t * (int64_t)K, K, raw);
+  constexpr bool kC = BPL > 0;                 // contiguous-lane rows
+  uint4 raw[kC ? 2 * BPL : NCH];
+  if (t < T) {
+    if constexpr (kC) load_bf16_c<BPL>(x + t * (int64_t)K, raw);
+    else load_bf16_raw<NCH>(x + t * (int64_t)K, K, raw);
+  }
 
   for (int e = tid; e < E; e += kQpThreads) { pre[0][e] = 0; pre[1][e] = 0; }
   __syncthreads();
@@ -577,12 +683,17 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
   // The token's codes do not depend on the routing: wavefronts 1..7 quantise
   // while wavefront 0 ranks the group's entries, then quantises its own.
   RowCodes<NCH> o;
+  RowCodesC<kC ? BPL : 1> oc;
   uint32_t sw[(NCH + 7) / 8];
   auto quantise = [&]() __attribute__((always_inline)) {
-    float v[NCH][8];
-    unpack_bf16<NCH>(raw, v);
-    quantize_lane_row<NCH>(v, o);
-    pack_scales<NCH>(o, sw);
+    if constexpr (kC) {
+      quantize_lane_row_c<BPL>(raw, oc);
+    } else {
+      float v[NCH][8];
+      unpack_bf16<NCH>(raw, v);
+      quantize_lane_row<NCH>(v, o);
+      pack_scales<NCH>(o, sw);
+    }
   };
   if (wave != 0 && t < T) quantise();
   if (wave == 0) {
@@ -624,7 +735,10 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
   const int my_row = lane < k ? rows[wave * k + lane] : -1;
   for (int slot = 0; slot < k; ++slot) {
     const int row = __shfl(my_row, slot, kWave);
-    if (row >= 0) store_row<NCH>(o, sw, K, row, codes, bscales, rscales);
+    if (row >= 0) {
+      if constexpr (kC) store_row_c<BPL>(oc, K, row, codes, bscales, rscales);
+      else store_row<NCH>(o, sw, K, row, codes, bscales, rscales);
+    }
   }
 }
 
@@ -787,17 +901,22 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
     // count per (chunk, expert), then offsets + rank + quantise + scatter
     route_count_kernel<<<pchunks, kPlanThreads, 0, s>>>(topk_ids, (int)n, E, table, dev_err);
     const unsigned grid = (unsigned)((T + kQpWaves - 1) / kQpWaves);
-    switch (nch_for(H)) {
-#define QP_LAUNCH(C)                                                                             \
-      case C:                                                                                    \
-        quantize_permute_kernel<C><<<grid, kQpThreads, 0, s>>>(x, T, (int)H, topk_ids, (int)k,   \
-            (int)E, table, pchunks, codes, bscales, rscales, expert_offsets, row_to_tk,          \
-            tk_to_row);                                                                          \
-        break;
-      QP_LAUNCH(1) QP_LAUNCH(2) QP_LAUNCH(4)
-      default: QP_LAUNCH(8)
-#undef QP_LAUNCH
+#define QP_LAUNCH(C, B)                                                                          \
+    quantize_permute_kernel<C, B><<<grid, kQpThreads, 0, s>>>(x, T, (int)H, topk_ids, (int)k,     \
+        (int)E, table, pchunks, codes, bscales, rscales, expert_offsets, row_to_tk, tk_to_row)
+    // rows of 1024, 2048 or 4096 elements: contiguous lanes; other lengths: strided lanes
+    if (H == 1024) QP_LAUNCH(2, 1);
+    else if (H == 2048) QP_LAUNCH(4, 2);
+    else if (H == 4096) QP_LAUNCH(8, 4);
+    else {
+      switch (nch_for(H)) {
+        case 1: QP_LAUNCH(1, 0); break;
+        case 2: QP_LAUNCH(2, 0); break;
+        case 4: QP_LAUNCH(4, 0); break;
+        default: QP_LAUNCH(8, 0); break;
+      }
     }
+#undef QP_LAUNCH
   } else {
     // long routing lists or long rows: plan over chunks of 1024 entries in many
     // workgroups (the last to arrive scans), then rank + quantise + scatter

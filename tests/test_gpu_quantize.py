@@ -122,6 +122,14 @@ def test_quantize_permute_ragged(T, E, k, kind):
     _check_permute(x, ids, E, f"{kind}")
 
 
+@pytest.mark.parametrize("H", [1024, 3072, 4096])
+def test_quantize_permute_row_lengths(H):
+    """Rows of 1024/2048/4096 elements take the contiguous-lane quantiser, others the strided one."""
+    x = W.activations(300, H, config=9, tensor=H)
+    ids, _ = W.make_routing("zipf", 300, 32, 4, config=9)
+    _check_permute(x, ids, 32, f"H={H}")
+
+
 def test_quantize_permute_long_rows():
     """H > 4096 takes the many-workgroup plan and the 1-token-per-wavefront pass."""
     x = W.activations(50, 8192, config=9, tensor=3)
