@@ -329,6 +329,20 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(
   store_row<NCH>(o, sw, K, row, codes, bscales, rscales);
 }
 
+// rows of 1024 * BPL elements with contiguous lanes
+template <int BPL>
+__global__ __launch_bounds__(256) void quantize_rows_c_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int K, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ bscales, float* __restrict__ rscales) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  uint4 raw[2 * BPL];
+  load_bf16_c<BPL>(x + row * (int64_t)K, raw);
+  RowCodesC<BPL> o;
+  quantize_lane_row_c<BPL>(raw, o);
+  store_row_c<BPL>(o, K, row, codes, bscales, rscales);
+}
+
 template <int NCH>
 __global__ __launch_bounds__(256) void quantize_rows_tiled_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int K, int64_t G, uint8_t* __restrict__ codes,
@@ -854,7 +868,14 @@ NVFP4MOE_API int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t K,
     return NVFP4_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  NVFP4_DISPATCH_NCH(K, quantize_rows_kernel, grid, s, x, rows, (int)K, codes, bscales, rscales);
+  if (K == 1024)
+    quantize_rows_c_kernel<1><<<grid, 256, 0, s>>>(x, rows, (int)K, codes, bscales, rscales);
+  else if (K == 2048)
+    quantize_rows_c_kernel<2><<<grid, 256, 0, s>>>(x, rows, (int)K, codes, bscales, rscales);
+  else if (K == 4096)
+    quantize_rows_c_kernel<4><<<grid, 256, 0, s>>>(x, rows, (int)K, codes, bscales, rscales);
+  else
+    NVFP4_DISPATCH_NCH(K, quantize_rows_kernel, grid, s, x, rows, (int)K, codes, bscales, rscales);
   return launch_status();
 }
 

@@ -35,7 +35,7 @@ def test_quantize_rows_tiny_config():
     _check_rows(W.gaussian_bf16((128, 256), 1.0, W.CFG_TINY, 1), "W 128x256")
 
 
-@pytest.mark.parametrize("K", [16, 48, 256, 512, 528, 768, 1040, 2048, 4096, 8192])
+@pytest.mark.parametrize("K", [16, 48, 256, 512, 528, 768, 1024, 1040, 2048, 4096, 8192])
 def test_quantize_rows_lengths(K):
     _check_rows(W.activations(37, K, config=2, tensor=K), f"K={K}")
 
