@@ -58,8 +58,8 @@ __global__ __launch_bounds__(256) void permute_gather_kernel(
     *reinterpret_cast<uint4*>(dst + base) = *reinterpret_cast<const uint4*>(src + base);
 }
 
-// Gradient of h = w * silu(g) * u; FP64 arithmetic in the order of the
-// definition, each output rounded once to bf16.
+// Gradient of h = w * silu(g) * u in float64 (sigmoid from a refined
+// reciprocal, silu = g * sigmoid), each output rounded once to bf16.
 __global__ __launch_bounds__(256) void swiglu_backward_kernel(
     const float* __restrict__ gu, const float* __restrict__ dh, int I,
     const int32_t* __restrict__ offsets, int E, const float* __restrict__ topk_w,
@@ -87,9 +87,8 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(
         const double g = gs[j + q], u = us[j + q];
         double t = ds[j + q];
         if (topk_w) t = t * (double)w;
-        const double den = 1.0 + exp(-g);
-        const double sig = 1.0 / den;
-        const double silu = g / den;
+        const double sig = recip_f64(1.0 + exp(-g));
+        const double silu = g * sig;
         const double du = t * silu;
         const double dg = (t * u) * (sig * (1.0 + g * (1.0 - sig)));
         bg[q] = f64_to_bf16_rne(dg);

@@ -91,11 +91,26 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double d) {
   int e;
   (void)__builtin_frexp(a, &e);            // a = m 2^e, m in [0.5, 1)
   if (e < -125) e = -125;                  // fixed step 2^-133 below 2^-126
-  double step = __builtin_ldexp(1.0, e - 8);
-  double r = __builtin_rint(a / step) * step;
+  // a / 2^(e-8) and back: exact scalings by powers of two
+  double r = __builtin_ldexp(__builtin_rint(__builtin_ldexp(a, 8 - e)), e - 8);
   float f = (float)r;                      // exact (<= 8 significant bits) or inf
   uint32_t bits = __float_as_uint(f) >> 16;
   return bits | (d < 0.0 ? 0x8000u : 0u);
+}
+
+// ------------------------------------------------------------------ float64 SwiGLU helpers
+// 1/d for float64 d >= 1 (or +inf, or NaN): the hardware estimate refined by
+// two Newton steps (the relative error squares at each step), within an ulp or
+// so of the quotient; 1/inf = 0; NaN propagates.  It replaces a float64
+// division where a result is rounded on to bf16: a few float64 ulps move the
+// bf16 result only next to a bf16 rounding midpoint.
+__device__ __forceinline__ double recip_f64(double d) {
+  if (!(d < __builtin_inf())) return d != d ? d : 0.0;
+  double y = __builtin_amdgcn_rcp(d);
+  double e = __builtin_fma(-d, y, 1.0);
+  y = __builtin_fma(y, e, y);
+  e = __builtin_fma(-d, y, 1.0);
+  return __builtin_fma(y, e, y);
 }
 
 // ------------------------------------------------------------------ host helpers

@@ -11,8 +11,15 @@
 // The two dgrad GEMMs of a MoE layer read 0.4 and 0.8 GB of BF16 weights, so
 // they are bound by memory, not by the matrix cores; the design keeps many
 // bytes in flight and reads every byte from L2 as few times as it can:
-//   * one 512-thread workgroup per CU, tile 256 rows x 256 columns (8
-//     wavefronts of 128 x 64), K-step 32;
+//   * one 512-thread workgroup per CU, tiles of up to 320 rows x 256 columns
+//     (8 wavefronts of up to 160 x 64; the two wavefront rows take alternate
+//     16-row groups), K-step 32.  The tile height (320, 256, 192, 128 or 64)
+//     is picked per launch from the routing: an expert of up to 320 rows then
+//     streams each weight slab once, while a skewed routing gets shorter tiles
+//     that spread its large experts over more workgroups;
+//   * the MFMA loop is compiled once per count of 16-row groups a wavefront
+//     holds, so a partial tile runs straight-line code with every fragment
+//     read issued before its MFMAs;
 //   * A rows and weight rows go from global memory straight into LDS
 //     (global_load_lds) in a 4-stage ring, three K-steps ahead; the load
 //     cursor runs on into the next tile, so the ring never drains;
@@ -26,23 +33,27 @@
 //     a wait for loads never has to cover them;
 //   * tiles are scheduled like the NVFP4 GEMM: persistent workgroups,
 //     XCD-contiguous ranges, m-tile major, expert rows from device offsets;
-//     row fragments past an expert's end are skipped.
+//     row groups past an expert's end are neither loaded nor multiplied.
 #include "common.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace nvfp4moe {
 namespace gb {
 
-// Tile BM x 256 (BM = 2 * WM: 256, or 128 when the grid would otherwise get
-// too few tiles), 8 wavefronts of WM x 64.
+// Tiles of up to BM x 256, 8 wavefronts of up to WM x 64; the tile height
+// (kHeights) is chosen per launch from the routing.
+constexpr int BM = 320, WM = BM / 2, FM = WM / 16;
 constexpr int BN = 256, BK = 32;
+constexpr int kNumHeights = 5;
+constexpr int kHeights[kNumHeights] = {320, 256, 192, 128, 64};
+constexpr int kTileCost = 96;                 // rows' worth of per-tile cost (see the kernel)
 constexpr int kWaves = 8, kThreads = kWaves * 64;
 constexpr int kLdsStages = 147456;            // LDS for the stage ring (144 KiB)
 constexpr int kRowB = BK * 2;                 // 64 bytes of a row per K-step
 constexpr int WN = 64, FN = WN / 16;          // wavefront columns: 4 MFMA 16x16 tiles
 constexpr int kWI = BN * kRowB / 1024 / kWaves;   // weight load instructions per wavefront per K-step (2)
-constexpr int kMaxBM = 256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -53,8 +64,7 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // A stage: the activation tile, [BM rows][4 chunks of 16 B] with chunks
 // XOR-swizzled by row, then the weight tile, [32 k][256 n] (KN) or like the
-// activations (NK).  As many stages as fit kLdsStages: 4 for BM = 256, 6 for
-// BM = 128.
+// activations (NK).  As many stages as fit kLdsStages: 4.
 struct Stage {
   uint8_t* a;
   uint8_t* w;
@@ -63,6 +73,7 @@ struct Stage {
 struct __align__(16) Smem {
   uint8_t ring[kLdsStages];
   int tile_start[NVFP4MOE_MAX_EXPERTS + 1];
+  int bm;
 };
 
 // physical 16-byte chunk of logical chunk c (0..3) of row r: rows r..r+15 of
@@ -98,12 +109,17 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   }
 }
 
+// fn(std::integral_constant<int, v>) for the v in Is... equal to n
+template <int... Is, typename Fn>
+__device__ __forceinline__ void dispatch_count(int n, std::integer_sequence<int, Is...>, Fn&& fn) {
+  (void)((n == Is ? (fn(std::integral_constant<int, Is>{}), true) : false) || ...);
+}
+
 struct Tile {
   int e, m0, rows, n0;
 };
 
-template <int BM>
-__device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_start, int E,
+__device__ __forceinline__ Tile tile_at(int L, int n_tiles, int bm, const int* tile_start, int E,
                                         const int32_t* __restrict__ offsets) {
   const int tm = L / n_tiles, tn = L - tm * n_tiles;
   int lo = 0, hi = E;
@@ -113,19 +129,19 @@ __device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_star
   }
   Tile t;
   t.e = __builtin_amdgcn_readfirstlane(lo);
-  t.m0 = __builtin_amdgcn_readfirstlane(offsets[t.e] + (tm - tile_start[t.e]) * BM);
-  t.rows = __builtin_amdgcn_readfirstlane(min(BM, offsets[t.e + 1] - t.m0));
+  t.m0 = __builtin_amdgcn_readfirstlane(offsets[t.e] + (tm - tile_start[t.e]) * bm);
+  t.rows = __builtin_amdgcn_readfirstlane(min(bm, offsets[t.e + 1] - t.m0));
   t.n0 = tn * BN;
   return t;
 }
 
-template <bool KN, int WM>
+template <bool KN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ offsets,
                               int E, const uint16_t* __restrict__ w, int N, int K,
                               float* __restrict__ c) {
-  constexpr int BM = 2 * WM, FM = WM / 16;
-  constexpr int kAI = BM * kRowB / 1024 / kWaves;   // A load instructions per wavefront per K-step
+  constexpr int kAF = BM / 16;                      // A load instructions per K-step (16 rows each)
+  constexpr int kAI = (kAF + kWaves - 1) / kWaves;  // ... per wavefront, at most
   constexpr int kStageB = (BM + BN) * kRowB;
   constexpr int kStages = kLdsStages / kStageB;
   static_assert(kStages >= 3 && (kStages - 2) * (kAI + kWI) <= 15, "stage ring");
@@ -135,11 +151,39 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
   const int wm = wave >> 2, wn = wave & 3;
   const int l16 = lane & 15, g = lane >> 4;
 
+  const int n_tiles = (N + BN - 1) / BN;
   if (wave == 0) {
+    // Tile height: the candidate with the smallest estimated critical path,
+    // (tiles per workgroup) x (height + kTileCost), the last term standing for
+    // a tile's cost that does not scale with its rows (the weight slab it
+    // streams).  Taller tiles read each expert's weights fewer times; shorter
+    // ones spread a skewed routing over more workgroups.  Ties go to the taller.
+    const int G = gridDim.x, xg = (G & 7) == 0 ? 8 : 1;
+    int best = kHeights[0];
+    int64_t best_cost = INT64_MAX;
+#pragma unroll
+    for (int c = 0; c < kNumHeights; ++c) {
+      const int h = kHeights[c];
+      int mt = 0;
+      for (int e0 = 0; e0 < E; e0 += kWave) {
+        const int e = e0 + lane;
+        int v = e < E ? (offsets[e + 1] - offsets[e] + h - 1) / h : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+        mt += v;
+      }
+      const int64_t total = (int64_t)mt * n_tiles;
+      const int64_t per = (total + xg - 1) / xg, wgs = G / xg;
+      const int64_t cost = (per + wgs - 1) / wgs * (h + kTileCost);
+      if (cost < best_cost) {
+        best_cost = cost;
+        best = h;
+      }
+    }
     int carry = 0;
     for (int e0 = 0; e0 < E; e0 += kWave) {
       const int e = e0 + lane;
-      const int v = e < E ? (offsets[e + 1] - offsets[e] + BM - 1) / BM : 0;
+      const int v = e < E ? (offsets[e + 1] - offsets[e] + best - 1) / best : 0;
       int incl = v;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
@@ -149,11 +193,14 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
       if (e < E) sm.tile_start[e] = carry + incl - v;
       carry += __shfl(incl, kWave - 1, kWave);
     }
-    if (lane == 0) sm.tile_start[E] = carry;
+    if (lane == 0) {
+      sm.tile_start[E] = carry;
+      sm.bm = best;
+    }
   }
   __syncthreads();
 
-  const int n_tiles = (N + BN - 1) / BN;
+  const int bm = __builtin_amdgcn_readfirstlane(sm.bm);
   const int total = __builtin_amdgcn_readfirstlane(sm.tile_start[E]) * n_tiles;
   int begin, end, step;
   if ((gridDim.x & 7) == 0) {
@@ -175,14 +222,19 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
   // offsets from the operand bases (the host keeps both under 4 GiB).  Instruction q
   // of an operand fills 1 KiB: A (and NK weight) rows 16q .. 16q+15, lane l ->
   // row 16q + l/4, physical chunk l%4; KN weight rows k = 2q, 2q+1, lane l ->
-  // k = 2q + l/32, columns 8 (l%32) .. +7.
+  // k = 2q + l/32, columns 8 (l%32) .. +7.  Wavefront v issues the A
+  // instructions q = v, v + 8, ... that hold rows of the tile (none past its
+  // last 16-row group) and the weight instructions 2v, 2v + 1.
   int lL = begin, lk = 0;
   uint32_t off_a[kAI], off_w[kWI];
+  int na = 0;   // A instructions of this wavefront for the load tile: q = wave + 8u < ceil(rows / 16)
   auto set_load_tile = [&](int L) __attribute__((always_inline)) {
-    const Tile t = tile_at<BM>(L, n_tiles, sm.tile_start, E, offsets);
+    const Tile t = tile_at(L, n_tiles, bm, sm.tile_start, E, offsets);
+    const int fa = min(kAF, (t.rows + 15) >> 4);
+    na = fa > wave ? (fa - wave + kWaves - 1) / kWaves : 0;
 #pragma unroll
     for (int u = 0; u < kAI; ++u) {
-      const int q = wave * kAI + u;
+      const int q = wave + kWaves * u;
       const int r = 16 * q + (lane >> 2);
       const int m = min(t.m0 + r, t.m0 + t.rows - 1);
       off_a[u] = ((uint32_t)m * K + 8 * swz(r, lane & 3)) * 2u;
@@ -211,7 +263,8 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
     const uint32_t ka = (uint32_t)lk * kRowB;
     const uint32_t kw = KN ? (uint32_t)lk * BK * N * 2u : (uint32_t)lk * kRowB;
 #pragma unroll
-    for (int u = 0; u < kAI; ++u) lds_dma16(a, off_a[u] + ka, S.a + (wave * kAI + u) * 1024);
+    for (int u = 0; u < kAI; ++u)
+      if (u < na) lds_dma16(a, off_a[u] + ka, S.a + (wave + kWaves * u) * 1024);
 #pragma unroll
     for (int u = 0; u < kWI; ++u) lds_dma16(w, off_w[u] + kw, S.w + (wave * kWI + u) * 1024);
     if (++lk == nk) {
@@ -219,7 +272,7 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
       lL += step;
       if (lL < end) set_load_tile(lL);
     }
-    return kAI + kWI;
+    return na + kWI;
   };
 
   floatx4 acc[FM][FN];
@@ -228,9 +281,11 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // one K-step of MFMAs from stage S; FULL: every row fragment holds rows
-  auto mma_step = [&](auto full_tag, int fm_eff, const Stage& S) __attribute__((always_inline)) {
-    constexpr bool FULL = decltype(full_tag)::value;
+  // one K-step of MFMAs from stage S over the wavefront's first NF row
+  // fragments (a compile-time count, so that every variant is straight-line
+  // code the compiler can schedule across fragments)
+  auto mma_step = [&](auto nf_tag, const Stage& S) __attribute__((always_inline)) {
+    constexpr int NF = decltype(nf_tag)::value;
     bf16x8 bv[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -255,25 +310,30 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
         bv[j] = *reinterpret_cast<const bf16x8*>(S.w + n * kRowB + swz(n, g) * 16);
       }
     }
+    // every fragment read is issued before the first MFMA (kept there by the
+    // scheduling barrier), so that the MFMAs wait on reads issued long before
+    bf16x8 av[FM];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if (FULL || i < fm_eff) {
-        const int r = WM * wm + 16 * i + l16;
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(S.a + r * kRowB + swz(r, g) * 16);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[j], av, acc[i][j], 0, 0, 0);
-      }
+    for (int i = 0; i < NF; ++i) {
+      const int r = 32 * i + 16 * wm + l16;
+      av[i] = *reinterpret_cast<const bf16x8*>(S.a + r * kRowB + swz(r, g) * 16);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NF; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[j], av[i], acc[i][j], 0, 0, 0);
   };
 
-  // C = acc^T: lane (l16, g) of tile (i, j) holds row 16i + l16, columns
-  // 16j + 4g .. +3 of the wavefront's block; rows past the tile's rows and
+  // C = acc^T: lane (l16, g) of tile (i, j) holds tile row 32i + 16wm + l16
+  // (the two wavefront rows take alternate 16-row groups, so a partial tile
+  // splits evenly), columns 16j + 4g .. +3 of the wavefront's 64; rows past the tile's rows and
   // columns past N are not written.  The accumulators are cleared.
   auto epilogue = [&](const Tile& t) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int r = WM * wm + 16 * i + l16;
+      const int r = 32 * i + 16 * wm + l16;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int n = t.n0 + WN * wn + 16 * j + 4 * g;
@@ -305,24 +365,24 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
     for (int i = 0; i < kStages - 2; ++i) nq[i] = nq[i + 1];
     nq[kStages - 2] = issue_loads(stage(sc == 0 ? kStages - 1 : sc - 1));
   };
-  auto run_tile = [&](auto full_tag, int fm_eff) __attribute__((always_inline)) {
-    mma_step(full_tag, fm_eff, stage(sc));   // K-step 0: its top is done by the caller
+  auto run_tile = [&](auto nf_tag) __attribute__((always_inline)) {
+    mma_step(nf_tag, stage(sc));   // K-step 0: its top is done by the caller
     sc = sc == kStages - 1 ? 0 : sc + 1;
     for (int kt = 1; kt < nk; ++kt) {
       top();
-      mma_step(full_tag, fm_eff, stage(sc));
+      mma_step(nf_tag, stage(sc));
       sc = sc == kStages - 1 ? 0 : sc + 1;
     }
   };
 
   Tile prev{0, 0, 0, 0};
   for (int L = begin; L < end; L += step) {
-    const Tile t = tile_at<BM>(L, n_tiles, sm.tile_start, E, offsets);
+    const Tile t = tile_at(L, n_tiles, bm, sm.tile_start, E, offsets);
     top();
     epilogue(prev);   // before the first tile: no rows, nothing is written
-    const int fm_eff = min(FM, max(0, (t.rows - WM * wm + 15) >> 4));
-    if (t.rows == BM) run_tile(std::true_type{}, FM);
-    else run_tile(std::false_type{}, fm_eff);
+    const int fm_eff = min(FM, (((t.rows + 15) >> 4) - wm + 1) >> 1);
+    dispatch_count(fm_eff, std::make_integer_sequence<int, FM + 1>{},
+                   [&](auto nf_tag) __attribute__((always_inline)) { run_tile(nf_tag); });
     prev = t;
   }
   epilogue(prev);
@@ -348,25 +408,20 @@ extern "C" NVFP4MOE_API int bf16_grouped_gemm(const uint16_t* a, const int32_t* 
   if (!a || !expert_offsets || !w || !c) return NVFP4_ERR_NULL;
   if (!aligned16(a) || !aligned16(w) || !aligned16(c)) return NVFP4_ERR_ALIGN;
   const int64_t n_tiles = (N + gb::BN - 1) / gb::BN;
-  // 256-row tiles when the expected tile count (the routing is on the device:
-  // about R/BM + E/2 row tiles) keeps the 256 workgroups busy for 4 rounds,
-  // else 128-row tiles
-  const bool tall = (R_cap / 256 + E / 2) * n_tiles >= 4 * 256;
-  const int64_t bm = tall ? 256 : 128;
-  const int64_t max_tiles = ((R_cap + bm - 1) / bm + E) * n_tiles;
+  // the most tiles any tile height can give (the kernel picks the height from
+  // the routing, which is on the device)
+  const int64_t min_h = gb::kHeights[gb::kNumHeights - 1];
+  const int64_t max_tiles = ((R_cap + min_h - 1) / min_h + E) * n_tiles;
   if (max_tiles > INT32_MAX) return NVFP4_ERR_SHAPE;
   // persistent grid: one workgroup per CU on a 256-CU device, a multiple of 8
   int64_t grid = max_tiles < 256 ? max_tiles : 256;
   if (grid >= 8) grid &= ~7ll;
   hipStream_t s = static_cast<hipStream_t>(stream);
-#define GB_LAUNCH(KN_, WM_)                                                                   \
-  gb::bf16_grouped_gemm_kernel<KN_, WM_><<<(unsigned)grid, gb::kThreads, 0, s>>>(             \
-      a, expert_offsets, E, w, (int)N, (int)K, c)
-  if (w_layout == NVFP4MOE_W_KN) {
-    if (tall) GB_LAUNCH(true, 128); else GB_LAUNCH(true, 64);
-  } else {
-    if (tall) GB_LAUNCH(false, 128); else GB_LAUNCH(false, 64);
-  }
-#undef GB_LAUNCH
+  if (w_layout == NVFP4MOE_W_KN)
+    gb::bf16_grouped_gemm_kernel<true><<<(unsigned)grid, gb::kThreads, 0, s>>>(
+        a, expert_offsets, E, w, (int)N, (int)K, c);
+  else
+    gb::bf16_grouped_gemm_kernel<false><<<(unsigned)grid, gb::kThreads, 0, s>>>(
+        a, expert_offsets, E, w, (int)N, (int)K, c);
   return launch_status();
 }
