@@ -145,7 +145,6 @@ def main():
           "rscales": torch.empty(R, dtype=torch.float32, device=dev)}
     dn = torch.empty(R, H, dtype=torch.float32, device=dev)
     y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
-    dy_perm = torch.empty(R, H, dtype=torch.bfloat16, device=dev)
     dh = torch.empty(R, I, dtype=torch.float32, device=dev)
     dgu = torch.empty(R, 2 * I, dtype=torch.bfloat16, device=dev)
     dx_perm = torch.empty(R, H, dtype=torch.float32, device=dev)
@@ -163,8 +162,9 @@ def main():
         ("swiglu_quantize", lambda: pmg.swiglu_quantize(gu, off, tw, perm["row_to_tk"], out=a2)),
         ("down_gemm", lambda: pmg.nvfp4_grouped_gemm(a2["codes"], a2["bscales"], a2["rscales"], off, *q_d, c=dn)),
         ("combine", lambda: pmg.unpermute_combine(dn, perm["tk_to_row"], k, y=y)),
-        ("dgrad_gather", lambda: pmg.permute_gather_bf16(dy, off, perm["row_to_tk"], k, out=dy_perm)),
-        ("dgrad_down_gemm", lambda: pmg.bf16_grouped_gemm(dy_perm, off, wd, pmg.W_KN, c=dh)),
+        # the output gradient's rows are gathered into expert order inside the GEMM's loads
+        ("dgrad_down_gemm", lambda: pmg.bf16_grouped_gemm_gather(dy, perm["row_to_tk"], k, off, wd, pmg.W_KN,
+                                                                 c=dh)),
         ("swiglu_backward", lambda: pmg.swiglu_backward(gu, dh, off, tw, perm["row_to_tk"], dgu=dgu)),
         ("dgrad_gate_up_gemm", lambda: pmg.bf16_grouped_gemm(dgu, off, wgu, pmg.W_KN, c=dx_perm)),
         ("dgrad_combine", lambda: pmg.unpermute_combine(dx_perm, perm["tk_to_row"], k, y=dx)),
@@ -214,7 +214,6 @@ def main():
         "quantize_permute": T * H * 2 + T * k * 4 + Rr * nvfp4_row(H) + 2 * Rr * 4 + (E + 1) * 4,
         "swiglu_quantize": Rr * 2 * I * 4 + Rr * 4 * 2 + Rr * nvfp4_row(I),
         "combine": Rr * H * 4 + T * k * 4 + T * H * 2,
-        "dgrad_gather": T * H * 2 + Rr * 4 + Rr * H * 2,
         "swiglu_backward": Rr * 2 * I * 4 + Rr * I * 4 + Rr * 8 + Rr * 2 * I * 2,
         "dgrad_combine": Rr * H * 4 + T * k * 4 + T * H * 2,
     }

@@ -227,10 +227,26 @@ NVFP4MOE_API int bf16_grouped_gemm(const uint16_t* a, const int32_t* expert_offs
                                    void* stream);
 
 /*
+ * bf16_grouped_gemm_gather - bf16_grouped_gemm whose left operand is gathered
+ * from token order (permute_gather_bf16 fused into the GEMM's loads):
+ *   c[r][n] = sum_k a[row_to_tk[r] / k][k'] * W_e[k'][n]   for r in expert e's rows
+ *   a bf16 bits [T][K] (e.g. the output gradient of the tokens);
+ *   row_to_tk int32 [R_cap] from nvfp4_quantize_permute; 1 <= k <= NVFP4MOE_MAX_TOPK.
+ * Other arguments, layouts and requirements as bf16_grouped_gemm, with the
+ * 4 GiB limit on T * K * 2.  A row_to_tk entry outside [0, T * k) reads a row
+ * of a clamped into [0, T) (a wrong result, never an access outside a).
+ */
+NVFP4MOE_API int bf16_grouped_gemm_gather(const uint16_t* a, int64_t T, const int32_t* row_to_tk,
+                                          int32_t k, const int32_t* expert_offsets, int32_t E,
+                                          int64_t R_cap, const uint16_t* w, int32_t w_layout,
+                                          int64_t N, int64_t K, float* c, void* stream);
+
+/*
  * swiglu_backward - gradient of h = w * silu(g) * u with respect to g and u:
  *   t = dh * w;  du = t * silu(g);  dg = (t * u) * (sig * (1 + g * (1 - sig)))
- * with sig = 1 / (1 + exp(-g)), silu(g) = g / (1 + exp(-g)), in FP64; each
- * result rounded once to bf16 (nearest even).
+ * with sig = 1 / (1 + exp(-g)), silu(g) = g / (1 + exp(-g)), in FP64 (sig from a
+ * Newton-refined reciprocal, silu = g * sig: within a few FP64 ulps of the
+ * quotients); each result rounded once to bf16 (nearest even).
  *   gu float [R_cap][2I] (forward gate_up output); dh float [R_cap][I]
  *   topk_w / row_to_tk as in swiglu_quantize (NULL topk_w: w = 1)
  *   dgu bf16 bits [R_cap][2I]: [0, I) = dg, [I, 2I) = du

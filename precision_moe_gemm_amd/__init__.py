@@ -61,6 +61,8 @@ SIGNATURES = {
     "unpermute_combine": ([_P, _I64, _I32, _I64, _P, _P, _P, _P], _c.c_int),
     "permute_gather_bf16": ([_P, _I64, _I64, _I32, _P, _I32, _P, _P, _P], _c.c_int),
     "bf16_grouped_gemm": ([_P, _P, _I32, _I64, _P, _I32, _I64, _I64, _P, _P], _c.c_int),
+    "bf16_grouped_gemm_gather": ([_P, _I64, _P, _I32, _P, _I32, _I64, _P, _I32, _I64, _I64, _P, _P],
+                                 _c.c_int),
     "swiglu_backward": ([_P, _P, _I64, _I64, _P, _I32, _P, _P, _P, _P], _c.c_int),
     "nvfp4moe_mfma_ceiling": ([_I64, _P, _P], _c.c_int),
 }
@@ -287,6 +289,29 @@ def bf16_grouped_gemm(a, expert_offsets, w, w_layout: int = W_KN, c=None):
     _req(c, "c", _F32)
     _check("bf16_grouped_gemm", load_library().bf16_grouped_gemm(
         _ptr(a), _ptr(expert_offsets), E, R_cap, _ptr(w), w_layout, N, K, _ptr(c), _stream()))
+    return c
+
+
+def bf16_grouped_gemm_gather(a, row_to_tk, k: int, expert_offsets, w, w_layout: int = W_KN, c=None):
+    """c[r] = a[row_to_tk[r] // k] @ W_e: the grouped GEMM over token rows gathered in its loads.
+
+    a bf16 [T, K]; row_to_tk int32 [R_cap].  Returns f32 [R_cap, N]."""
+    _req(a, "a", _BF16, 2)
+    _req(row_to_tk, "row_to_tk", _I32T)
+    _req(expert_offsets, "expert_offsets", _I32T)
+    _req(w, "w", _BF16, 3)
+    T, K = a.shape
+    R_cap = row_to_tk.numel()
+    E = expert_offsets.numel() - 1
+    N = w.shape[2] if w_layout == W_KN else w.shape[1]
+    kw = w.shape[1] if w_layout == W_KN else w.shape[2]
+    if kw != K or w.shape[0] != E:
+        raise ValueError("weight shape does not match a / expert_offsets")
+    c = _empty((R_cap, N), torch.float32, a) if c is None else c
+    _req(c, "c", _F32)
+    _check("bf16_grouped_gemm_gather", load_library().bf16_grouped_gemm_gather(
+        _ptr(a), T, _ptr(row_to_tk), k, _ptr(expert_offsets), E, R_cap, _ptr(w), w_layout, N, K,
+        _ptr(c), _stream()))
     return c
 
 

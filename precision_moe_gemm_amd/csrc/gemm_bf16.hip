@@ -137,7 +137,8 @@ __device__ __forceinline__ Tile tile_at(int L, int n_tiles, int bm, const int* t
 
 template <bool KN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ offsets,
+void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_map,
+                              int a_div, int a_rows, const int32_t* __restrict__ offsets,
                               int E, const uint16_t* __restrict__ w, int N, int K,
                               float* __restrict__ c) {
   constexpr int kAF = BM / 16;                      // A load instructions per K-step (16 rows each)
@@ -236,7 +237,10 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
     for (int u = 0; u < kAI; ++u) {
       const int q = wave + kWaves * u;
       const int r = 16 * q + (lane >> 2);
-      const int m = min(t.m0 + r, t.m0 + t.rows - 1);
+      int m = min(t.m0 + r, t.m0 + t.rows - 1);
+      // gathered operand: routed row m reads row a_map[m] / a_div of a,
+      // clamped into a (an invalid map entry reads a wrong row, never outside)
+      if (a_map) m = min(max(a_map[m], 0) / a_div, a_rows - 1);
       off_a[u] = ((uint32_t)m * K + 8 * swz(r, lane & 3)) * 2u;
     }
 #pragma unroll
@@ -393,18 +397,21 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
 
 using namespace nvfp4moe;
 
-extern "C" NVFP4MOE_API int bf16_grouped_gemm(const uint16_t* a, const int32_t* expert_offsets,
-                                              int32_t E, int64_t R_cap, const uint16_t* w,
-                                              int32_t w_layout, int64_t N, int64_t K, float* c,
-                                              void* stream) {
+namespace {
+
+int launch_bf16_grouped_gemm(const uint16_t* a, int64_t a_rows, const int32_t* a_map, int32_t a_div,
+                             const int32_t* expert_offsets, int32_t E, int64_t R_cap,
+                             const uint16_t* w, int32_t w_layout, int64_t N, int64_t K, float* c,
+                             void* stream) {
   if (w_layout != NVFP4MOE_W_KN && w_layout != NVFP4MOE_W_NK) return NVFP4_ERR_ARG;
-  if (E < 1 || E > NVFP4MOE_MAX_EXPERTS || R_cap < 0) return NVFP4_ERR_SHAPE;
+  if (E < 1 || E > NVFP4MOE_MAX_EXPERTS || R_cap < 0 || a_rows < 0) return NVFP4_ERR_SHAPE;
   if (K <= 0 || K % gb::BK != 0 || N < 16 || N % 16 != 0) return NVFP4_ERR_SHAPE;
   // the kernel addresses both operands with 32-bit byte offsets
-  if (R_cap * K * 2 > (int64_t)UINT32_MAX || (int64_t)E * N * K * 2 > (int64_t)UINT32_MAX ||
+  if (a_rows * K * 2 > (int64_t)UINT32_MAX || (int64_t)E * N * K * 2 > (int64_t)UINT32_MAX ||
       R_cap > INT32_MAX / 2)
     return NVFP4_ERR_SHAPE;
   if (R_cap == 0) return NVFP4_OK;
+  if (a_rows == 0) return NVFP4_ERR_SHAPE;   // routed rows but nothing to read them from
   if (!a || !expert_offsets || !w || !c) return NVFP4_ERR_NULL;
   if (!aligned16(a) || !aligned16(w) || !aligned16(c)) return NVFP4_ERR_ALIGN;
   const int64_t n_tiles = (N + gb::BN - 1) / gb::BN;
@@ -419,9 +426,31 @@ extern "C" NVFP4MOE_API int bf16_grouped_gemm(const uint16_t* a, const int32_t* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w_layout == NVFP4MOE_W_KN)
     gb::bf16_grouped_gemm_kernel<true><<<(unsigned)grid, gb::kThreads, 0, s>>>(
-        a, expert_offsets, E, w, (int)N, (int)K, c);
+        a, a_map, a_div, (int)a_rows, expert_offsets, E, w, (int)N, (int)K, c);
   else
     gb::bf16_grouped_gemm_kernel<false><<<(unsigned)grid, gb::kThreads, 0, s>>>(
-        a, expert_offsets, E, w, (int)N, (int)K, c);
+        a, a_map, a_div, (int)a_rows, expert_offsets, E, w, (int)N, (int)K, c);
   return launch_status();
+}
+
+}  // namespace
+
+extern "C" NVFP4MOE_API int bf16_grouped_gemm(const uint16_t* a, const int32_t* expert_offsets,
+                                              int32_t E, int64_t R_cap, const uint16_t* w,
+                                              int32_t w_layout, int64_t N, int64_t K, float* c,
+                                              void* stream) {
+  return launch_bf16_grouped_gemm(a, R_cap, nullptr, 1, expert_offsets, E, R_cap, w, w_layout, N, K,
+                                  c, stream);
+}
+
+extern "C" NVFP4MOE_API int bf16_grouped_gemm_gather(const uint16_t* a, int64_t T,
+                                                     const int32_t* row_to_tk, int32_t k,
+                                                     const int32_t* expert_offsets, int32_t E,
+                                                     int64_t R_cap, const uint16_t* w,
+                                                     int32_t w_layout, int64_t N, int64_t K,
+                                                     float* c, void* stream) {
+  if (k < 1 || k > NVFP4MOE_MAX_TOPK) return NVFP4_ERR_SHAPE;
+  if (R_cap > 0 && !row_to_tk) return NVFP4_ERR_NULL;
+  return launch_bf16_grouped_gemm(a, T, row_to_tk, k, expert_offsets, E, R_cap, w, w_layout, N, K,
+                                  c, stream);
 }

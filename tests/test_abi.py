@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
     for n in ("nvfp4_quantize_permute", "nvfp4_grouped_gemm", "swiglu_quantize", "unpermute_combine",
-              "nvfp4_quantize_rows", "bf16_grouped_gemm", "permute_gather_bf16", "swiglu_backward"):
+              "nvfp4_quantize_rows", "bf16_grouped_gemm", "bf16_grouped_gemm_gather", "permute_gather_bf16",
+              "swiglu_backward"):
         assert n in names
 
 
@@ -93,6 +94,16 @@ def test_gemm_host_checks(lib):
     g = lib.bf16_grouped_gemm
     assert g(FAKE, FAKE, 128, 32768, FAKE, 7, 768, 2048, FAKE, None) == ERR_ARG
     assert g(FAKE, FAKE, 128, 32768, FAKE, 0, 768, 2040, FAKE, None) == ERR_SHAPE
+    gg = lib.bf16_grouped_gemm_gather
+    #        a     T     map   k  offsets E    R_cap  w    lay N    K     c     stream
+    assert gg(FAKE, 4096, FAKE, 0, FAKE, 128, 32768, FAKE, 0, 768, 2048, FAKE, None) == ERR_SHAPE
+    assert gg(FAKE, 4096, FAKE, 33, FAKE, 128, 32768, FAKE, 0, 768, 2048, FAKE, None) == ERR_SHAPE
+    assert gg(FAKE, 4096, None, 8, FAKE, 128, 32768, FAKE, 0, 768, 2048, FAKE, None) == ERR_NULL
+    assert gg(FAKE, 0, FAKE, 8, FAKE, 128, 32768, FAKE, 0, 768, 2048, FAKE, None) == ERR_SHAPE
+    assert gg(FAKE, 1 << 21, FAKE, 8, FAKE, 128, 32768, FAKE, 0, 768, 2048, FAKE, None) == ERR_SHAPE  # 4 GiB
+    assert gg(FAKE, 4096, FAKE, 8, FAKE, 128, 32768, FAKE, 3, 768, 2048, FAKE, None) == ERR_ARG
+    assert gg(FAKE + 4, 4096, FAKE, 8, FAKE, 128, 32768, FAKE, 0, 768, 2048, FAKE, None) == ERR_ALIGN
+    assert gg(None, 0, None, 8, None, 128, 0, None, 0, 768, 2048, None, None) == OK
 
 
 def test_quantize_rows_tiled_host_checks(lib):

@@ -160,3 +160,25 @@ def test_bf16_dgrad_shapes_sampled(K, N, kind):
     rows, _ = sample_rows(off, [0, 64, 127], extra=5, seed=4)
     ref, bound = og.bf16_grouped_gemm_ref(of.bf16_to_f32(a), off, of.bf16_to_f32(w), trans_w=False, rows=rows)
     print("  err/bound", assert_within(c[rows], ref, bound, "dgrad"))
+
+
+@pytest.mark.parametrize("T,E,k,K,N,kind", [(4096, 128, 8, 2048, 768, "softmax"),
+                                             (40, 16, 2, 96, 64, "zipf")])
+def test_bf16_grouped_gemm_gather(T, E, k, K, N, kind):
+    """The gathered-operand GEMM equals the GEMM of the gathered rows bit for bit, and the oracle."""
+    print(f"[bf16 gemm gather] T={T} E={E} k={k} K={K} N={N} {kind}", flush=True)
+    ids, tw, off, r2t, t2r = _routing(T, E, k, kind, 65)
+    x = W.gaussian_bf16((T, K), 1.0, 65, 38)
+    w = W.gaussian_bf16((E, K, N), 0.02, 65, 39)
+    xd, wd, offd, r2td = bf16_dev(x), bf16_dev(w), dev(off), dev(r2t)
+    c = host(pmg.bf16_grouped_gemm_gather(xd, r2td, k, offd, wd))
+    c2 = host(pmg.bf16_grouped_gemm(pmg.permute_gather_bf16(xd, offd, r2td, k), offd, wd))
+    Rv = int(off[-1])
+    assert np.array_equal(c[:Rv].view(np.uint32), c2[:Rv].view(np.uint32))
+    a_perm = of.bf16_to_f32(x)[r2t[:Rv] // k]
+    if T * k > 1000:
+        rows, _ = sample_rows(off, [0, E - 1], extra=3, seed=5)
+    else:
+        rows = np.arange(Rv)
+    ref, bound = og.bf16_grouped_gemm_ref(a_perm, off, of.bf16_to_f32(w), trans_w=False, rows=rows)
+    print("  err/bound", assert_within(c[rows], ref, bound, "gather gemm"))
