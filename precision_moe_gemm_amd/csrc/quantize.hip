@@ -544,111 +544,143 @@ __global__ __launch_bounds__(256) void quantize_route_kernel(
 
 // Route + permute + quantise in two launches.
 //
-// The count: one 1024-thread workgroup per chunk of 4096 routing entries
-// counts the chunk's entries per expert in LDS and writes the counts,
-// cnt[c][e].  Workgroups are independent, so the pass costs one load round
-// trip.  Used while nchunks * E <= kCountTable (the main pass reads the whole
-// table in every workgroup).
+// The rank pass: workgroup c (16 wavefronts) takes chunk c of 4096 routing
+// entries.  Each wavefront ranks its 256 entries in 4 passes of 64
+// consecutive ones by ballot matching on the expert id, keeping a running
+// count per expert in LDS; an exclusive scan of those counts over the
+// wavefronts gives every entry its stable rank among the chunk's entries of
+// its expert (entry order: token, then slot).  The ranks go to the workspace
+// and the chunk's counts per expert to the table, cnt[c][e].  Workgroups are
+// independent; the launch boundary publishes the results.
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kPlanChunkLog = 12;        // 4096 routing entries per chunk
-constexpr int kCountTable = 4096;        // ints of (chunk, expert) counts the main pass reads
+constexpr int kPlanChunk = 1 << kPlanChunkLog;
+constexpr int kCountTable = 4096;        // ints of (chunk, expert) counts the main pass scans
 
-inline int plan_chunks(int64_t n) { return n > 0 ? (int)((n + (1 << kPlanChunkLog) - 1) >> kPlanChunkLog) : 1; }
+inline int plan_chunks(int64_t n) { return n > 0 ? (int)((n + kPlanChunk - 1) >> kPlanChunkLog) : 1; }
 
-__global__ __launch_bounds__(kPlanThreads) void route_count_kernel(
+__global__ __launch_bounds__(kPlanThreads) void route_rank_kernel(
     const int32_t* __restrict__ ids, int n, int E, int32_t* __restrict__ cnt_out,
-    int32_t* __restrict__ dev_err) {
-  __shared__ int32_t cnt[NVFP4MOE_MAX_EXPERTS];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kPlanThreads) cnt[e] = 0;
-  __syncthreads();
-  const int i0 = (blockIdx.x << kPlanChunkLog) + 4 * tid;   // 4 entries per thread
-  int v[4];
-  if (i0 + 3 < n && (reinterpret_cast<uintptr_t>(ids) & 15) == 0) {
-    const int4 q = *reinterpret_cast<const int4*>(ids + i0);
-    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-  } else {
+    int32_t* __restrict__ rank_out, int32_t* __restrict__ dev_err) {
+  __shared__ int32_t wcnt[kPlanWaves][NVFP4MOE_MAX_EXPERTS];   // per wavefront, then its exclusive prefix
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int base = (blockIdx.x << kPlanChunkLog) + wave * 256;   // this wavefront's 256 entries
+  int ev[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = i0 + u < n ? ids[i0 + u] : 0;
+  for (int u = 0; u < 4; ++u) {
+    const int i = base + 64 * u + lane;
+    ev[u] = i < n ? ids[i] : -1;
   }
+  for (int e = lane; e < E; e += kWave) wcnt[wave][e] = 0;   // each wavefront clears its own row
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int lr[4];
   bool bad = false;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    if (i0 + u >= n) continue;
-    if (v[u] >= 0 && v[u] < E) atomicAdd(&cnt[v[u]], 1);
-    else bad = true;
+    const int i = base + 64 * u + lane;
+    const int e = ev[u];
+    const bool valid = i < n && e >= 0 && e < E;
+    bad |= i < n && !valid;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t bb = __ballot(bit);
+      peers &= bit ? bb : ~bb;
+    }
+    lr[u] = -1;
+    if (valid) {
+      const int r = __popcll(peers & lt_mask);
+      const int before = wcnt[wave][e];
+      lr[u] = before + r;
+      if (r == 0) wcnt[wave][e] = before + __popcll(peers);
+    }
   }
   if (bad && dev_err) atomicOr(dev_err, NVFP4_DEVERR_BAD_EXPERT);
   __syncthreads();
-  for (int e = tid; e < E; e += kPlanThreads) cnt_out[blockIdx.x * E + e] = cnt[e];
+  // exclusive scan over the wavefronts, per expert; the chunk's counts
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int acc = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanWaves; ++w) {
+      const int v = wcnt[w][e];
+      wcnt[w][e] = acc;
+      acc += v;
+    }
+    cnt_out[blockIdx.x * E + e] = acc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = base + 64 * u + lane;
+    if (i < n) rank_out[i] = lr[u] >= 0 ? wcnt[wave][ev[u]] + lr[u] : -1;
+  }
 }
 
 // The main pass.  Workgroup w (8 wavefronts) owns tokens [8w, 8w + 8), one
-// per wavefront.  Its activations, the count table and every routing id it
-// needs (its own entries, and its chunk's entries before them, at most 4095)
-// are loaded at the start.  From the table it forms the expert offsets and
-// the first row of each expert in its chunk(s); it counts per expert the
-// chunk's entries before its first one, ranks its own entries in (token, slot)
-// order by ballot matching, and so places every entry.  Each token is
-// quantised once and written to its k rows.  Workgroup 0 also writes the
-// expert offsets.
+// per wavefront.  Every load it needs is issued at the start: the token's
+// activations, its k expert ids and ranks, and the count table.  The token is
+// quantised first (its codes do not depend on the routing); the workgroup
+// then forms, from the table, the expert offsets and the first row of each
+// expert in the chunk(s) its entries fall in, and an entry's row is that
+// first row plus its rank.  Each token is written to its k rows.  Workgroup 0
+// also writes the expert offsets.
 constexpr int kQpWaves = 8;
 constexpr int kQpThreads = kQpWaves * 64;
-constexpr int kQpPre = (1 << kPlanChunkLog) / kQpThreads;   // prefix ids per thread (8)
 constexpr int kQpExp = NVFP4MOE_MAX_EXPERTS / kQpThreads;   // experts per thread (2)
 
 template <int NCH, int BPL>
 __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
     const uint16_t* __restrict__ x, int64_t T, int K, const int32_t* __restrict__ ids, int k, int E,
-    const int32_t* __restrict__ cnt, int nchunks, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ bscales, float* __restrict__ rscales, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ row_to_tk, int32_t* __restrict__ tk_to_row) {
-  __shared__ int32_t pre[2][NVFP4MOE_MAX_EXPERTS];     // chunk entries before e0, per part
-  __shared__ int32_t sbase[2][NVFP4MOE_MAX_EXPERTS];   // first row of expert e in part's chunk
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ rank, int nchunks,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales, float* __restrict__ rscales,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_to_tk, int32_t* __restrict__ tk_to_row) {
+  __shared__ int32_t sbase[2][NVFP4MOE_MAX_EXPERTS];   // first row of expert e in chunk c0, c0 + 1
   __shared__ int32_t wsum[kQpWaves];
-  __shared__ int32_t rows[kQpWaves * NVFP4MOE_MAX_TOPK];
   __shared__ int32_t tab[kCountTable];                  // the count table
   const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int64_t t = (int64_t)blockIdx.x * kQpWaves + wave;
-  const int n = (int)(T * k);
   const int e0 = (int)((int64_t)blockIdx.x * kQpWaves * k);       // first entry of the group
-  const int e1 = min(e0 + kQpWaves * k, n);                        // one past the last
-  const int cs = (e0 >> kPlanChunkLog) << kPlanChunkLog;          // start of e0's chunk
-  const int second = cs + (1 << kPlanChunkLog);                    // start of the next chunk
-  const int c0 = e0 >> kPlanChunkLog;                              // e0's chunk
+  const int c0 = e0 >> kPlanChunkLog;                              // its chunk
 
-  // the count table, into LDS (independent loads, all in flight together)
-#pragma unroll
-  for (int u = 0; u < kCountTable / kQpThreads; ++u) {
-    const int i = u * kQpThreads + tid;
-    if (i < nchunks * E) tab[i] = cnt[i];
-  }
-  // the chunk's ids before e0 (strided over the workgroup) and, in wavefront
-  // 0, the group's own ids
-  int pv[kQpPre];
-#pragma unroll
-  for (int u = 0; u < kQpPre; ++u) {
-    const int i = cs + u * kQpThreads + tid;
-    pv[u] = i < e0 ? ids[i] : -1;
-  }
-  int own[(kQpWaves * NVFP4MOE_MAX_TOPK) / kWave];
-#pragma unroll
-  for (int u = 0; u < (kQpWaves * NVFP4MOE_MAX_TOPK) / kWave; ++u) {
-    const int idx = e0 + u * kWave + lane;
-    own[u] = (wave == 0 && idx < e1) ? ids[idx] : -1;
-  }
-  // the token's activations last: waiting for the ids above does not wait for them
+  // every load first: activations, this token's entries, the count table
   constexpr bool kC = BPL > 0;                 // contiguous-lane rows
   uint4 raw[kC ? 2 * BPL : NCH];
   if (t < T) {
     if constexpr (kC) load_bf16_c<BPL>(x + t * (int64_t)K, raw);
     else load_bf16_raw<NCH>(x + t * (int64_t)K, K, raw);
   }
-
-  for (int e = tid; e < E; e += kQpThreads) { pre[0][e] = 0; pre[1][e] = 0; }
+  int my_e = -1, my_r = -1;
+  const int my_i = (int)(t * k) + lane;
+  if (t < T && lane < k) {
+    my_e = ids[my_i];
+    my_r = rank[my_i];
+  }
+  int tv[kCountTable / kQpThreads];             // the table, 8 independent loads per thread
+#pragma unroll
+  for (int u = 0; u < kCountTable / kQpThreads; ++u) {
+    const int i = u * kQpThreads + tid;
+    tv[u] = i < nchunks * E ? cnt[i] : 0;
+  }
+  // the token's codes
+  RowCodes<NCH> o;
+  RowCodesC<kC ? BPL : 1> oc;
+  uint32_t sw[(NCH + 7) / 8];
+  if (t < T) {
+    if constexpr (kC) {
+      quantize_lane_row_c<BPL>(raw, oc);
+    } else {
+      float v[NCH][8];
+      unpack_bf16<NCH>(raw, v);
+      quantize_lane_row<NCH>(v, o);
+      pack_scales<NCH>(o, sw);
+    }
+  }
+  // the table: per expert the total and the entries in chunks before c0, c0 + 1
+#pragma unroll
+  for (int u = 0; u < kCountTable / kQpThreads; ++u) tab[u * kQpThreads + tid] = tv[u];
   __syncthreads();
-  // per expert (thread tid owns experts 2 tid, 2 tid + 1): the total, and the
-  // entries in the chunks before c0 and before c0 + 1
   int tot[kQpExp], b0[kQpExp], b1[kQpExp];
 #pragma unroll
   for (int u = 0; u < kQpExp; ++u) { tot[u] = 0; b0[u] = 0; b1[u] = 0; }
@@ -688,70 +720,123 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
     off_e += tot[u];
   }
   if (blockIdx.x == 0 && tid == kQpThreads - 1) offsets[E] = before + incl;
-#pragma unroll
-  for (int u = 0; u < kQpPre; ++u) {
-    const int e = pv[u];
-    if (e >= 0 && e < E) atomicAdd(&pre[0][e], 1);
-  }
   __syncthreads();
-  // The token's codes do not depend on the routing: wavefronts 1..7 quantise
-  // while wavefront 0 ranks the group's entries, then quantises its own.
+  if (t >= T) return;
+  int row = -1;
+  if (lane < k) {
+    if (my_r >= 0) row = sbase[(my_i >> kPlanChunkLog) - c0][my_e] + my_r;
+    tk_to_row[my_i] = row;
+    if (row >= 0) row_to_tk[row] = my_i;
+  }
+  for (int slot = 0; slot < k; ++slot) {
+    const int r = __shfl(row, slot, kWave);
+    if (r >= 0) {
+      if constexpr (kC) store_row_c<BPL>(oc, K, r, codes, bscales, rscales);
+      else store_row<NCH>(o, sw, K, r, codes, bscales, rscales);
+    }
+  }
+}
+
+// Long routing lists (a count table too large for every workgroup of the
+// main pass to scan): the ranks as above, then one workgroup turns the table
+// into first rows,
+//   base[c][e] = offsets[e] + (entries of e in chunks before c),
+// in place and writes the offsets; the main pass then needs no scan at all.
+constexpr int64_t kMaxPlanTable = 1 << 20;   // chunks x experts (4 MiB of table)
+
+__global__ __launch_bounds__(kPlanThreads) void route_scan_kernel(
+    int32_t* __restrict__ table, int nchunks, int E, int32_t* __restrict__ offsets) {
+  __shared__ int32_t part[kPlanThreads];
+  __shared__ int32_t wsum[kPlanWaves];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  // thread (e, p), P = 1024 / E threads per expert, sums chunks [p cpt, (p + 1) cpt)
+  const int P = kPlanThreads / E, cpt = (nchunks + P - 1) / P;
+  const int e = tid / P, p = tid - e * P;
+  const int c_lo = min(nchunks, p * cpt), c_hi = min(nchunks, (p + 1) * cpt);
+  int sum = 0;
+  if (e < E)
+    for (int c = c_lo; c < c_hi; ++c) sum += table[(int64_t)c * E + e];
+  part[tid] = sum;
+  __syncthreads();
+  int pre_p = 0, tot = 0;
+  if (e < E) {
+    for (int q = 0; q < P; ++q) {
+      const int v = part[e * P + q];
+      if (q < p) pre_p += v;
+      tot += v;
+    }
+  }
+  // offsets: exclusive scan over experts of the totals, carried by thread (e, 0)
+  const int mine = (e < E && p == 0) ? tot : 0;
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();   // also: every read of part[] above is done
+  int wbefore = 0;
+  for (int w = 0; w < wave; ++w) wbefore += wsum[w];
+  if (e < E && p == 0) part[e] = wbefore + incl - mine;
+  __syncthreads();
+  if (e < E) {
+    const int off_e = part[e];
+    if (p == 0) offsets[e] = off_e;
+    int acc = off_e + pre_p;
+    for (int c = c_lo; c < c_hi; ++c) {
+      const int64_t at = (int64_t)c * E + e;
+      const int v = table[at];
+      table[at] = acc;
+      acc += v;
+    }
+  }
+  if (tid == kPlanThreads - 1) offsets[E] = wbefore + incl;
+}
+
+// Main pass over first rows: one wavefront per token, independent of every
+// other.  Lanes s < k read entry t k + s (expert id and rank) and the first
+// row of its expert in its chunk; the token is quantised once and written to
+// its k rows.
+constexpr int kQrWaves = 4;
+
+template <int NCH, int BPL>
+__global__ __launch_bounds__(kQrWaves * 64) void quantize_permute_rows_kernel(
+    const uint16_t* __restrict__ x, int64_t T, int K, const int32_t* __restrict__ ids, int k, int E,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ rank, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ bscales, float* __restrict__ rscales, int32_t* __restrict__ row_to_tk,
+    int32_t* __restrict__ tk_to_row) {
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * kQrWaves + wave;
+  if (t >= T) return;
+  constexpr bool kC = BPL > 0;                 // contiguous-lane rows
+  uint4 raw[kC ? 2 * BPL : NCH];
+  if constexpr (kC) load_bf16_c<BPL>(x + t * (int64_t)K, raw);
+  else load_bf16_raw<NCH>(x + t * (int64_t)K, K, raw);
+  int row = -1;
+  if (lane < k) {
+    const int i = (int)(t * k) + lane;
+    const int e = ids[i], r = rank[i];
+    if (r >= 0) row = base[(int64_t)(i >> kPlanChunkLog) * E + e] + r;
+    tk_to_row[i] = row;
+    if (row >= 0) row_to_tk[row] = i;
+  }
   RowCodes<NCH> o;
   RowCodesC<kC ? BPL : 1> oc;
   uint32_t sw[(NCH + 7) / 8];
-  auto quantise = [&]() __attribute__((always_inline)) {
-    if constexpr (kC) {
-      quantize_lane_row_c<BPL>(raw, oc);
-    } else {
-      float v[NCH][8];
-      unpack_bf16<NCH>(raw, v);
-      quantize_lane_row<NCH>(v, o);
-      pack_scales<NCH>(o, sw);
-    }
-  };
-  if (wave != 0 && t < T) quantise();
-  if (wave == 0) {
-    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-#pragma unroll
-    for (int u = 0; u < (kQpWaves * NVFP4MOE_MAX_TOPK) / kWave; ++u) {
-      const int i0 = e0 + u * kWave;
-      if (i0 >= e1) break;
-      const int idx = i0 + lane;
-      const int e = own[u];
-      const bool valid = idx < e1 && e >= 0 && e < E;
-      const int part = idx >= second ? 1 : 0;
-      uint64_t peers = __ballot(valid);
-      const uint64_t pb = __ballot(valid && part);
-      peers &= part ? pb : ~pb;
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = valid && ((e >> b) & 1);
-        const uint64_t bb = __ballot(bit);
-        peers &= bit ? bb : ~bb;
-      }
-      const int r = __popcll(peers & lt_mask);
-      int row = -1;
-      if (valid) {
-        const int bef = pre[part][e];
-        row = sbase[part][e] + bef + r;
-        if (r == 0) pre[part][e] = bef + __popcll(peers);
-      }
-      if (idx < e1) {
-        tk_to_row[idx] = row;
-        rows[idx - e0] = row;
-        if (valid) row_to_tk[row] = idx;
-      }
-    }
-    if (t < T) quantise();
+  if constexpr (kC) {
+    quantize_lane_row_c<BPL>(raw, oc);
+  } else {
+    float v[NCH][8];
+    unpack_bf16<NCH>(raw, v);
+    quantize_lane_row<NCH>(v, o);
+    pack_scales<NCH>(o, sw);
   }
-  __syncthreads();
-  if (t >= T) return;
-  const int my_row = lane < k ? rows[wave * k + lane] : -1;
   for (int slot = 0; slot < k; ++slot) {
-    const int row = __shfl(my_row, slot, kWave);
-    if (row >= 0) {
-      if constexpr (kC) store_row_c<BPL>(oc, K, row, codes, bscales, rscales);
-      else store_row<NCH>(o, sw, K, row, codes, bscales, rscales);
+    const int r = __shfl(row, slot, kWave);
+    if (r >= 0) {
+      if constexpr (kC) store_row_c<BPL>(oc, K, r, codes, bscales, rscales);
+      else store_row<NCH>(o, sw, K, r, codes, bscales, rscales);
     }
   }
 }
@@ -855,7 +940,11 @@ NVFP4MOE_API int nvfp4moe_abi_version(void) { return NVFP4MOE_ABI_VERSION; }
 
 NVFP4MOE_API size_t nvfp4moe_permute_workspace_size(int64_t T, int32_t k, int32_t E) {
   if (T < 0 || k <= 0 || E <= 0) return 0;
-  const size_t bytes = kPlanArrivalBytes + (size_t)route_chunks(T, k) * (size_t)E * sizeof(int32_t);
+  // the larger of the two plans: (chunk, expert) counts of 1024-entry chunks,
+  // or of 4096-entry chunks plus a rank per routing entry
+  const int64_t n = T * (int64_t)k;
+  const int64_t ints = std::max<int64_t>(route_chunks(T, k) * E, (int64_t)plan_chunks(n) * E + n);
+  const size_t bytes = kPlanArrivalBytes + (size_t)ints * sizeof(int32_t);
   return (bytes + 255) & ~(size_t)255;
 }
 
@@ -919,12 +1008,15 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
   int32_t* table = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + kPlanArrivalBytes);
   const int pchunks = plan_chunks(n);
   if (T > 0 && (int64_t)pchunks * E <= kCountTable && n <= INT32_MAX / 2 && H <= 4096) {
-    // count per (chunk, expert), then offsets + rank + quantise + scatter
-    route_count_kernel<<<pchunks, kPlanThreads, 0, s>>>(topk_ids, (int)n, E, table, dev_err);
+    // rank every entry within its chunk and expert and count per (chunk,
+    // expert); then offsets + rows + quantise + scatter
+    int32_t* rank = table + (int64_t)pchunks * E;
+    route_rank_kernel<<<pchunks, kPlanThreads, 0, s>>>(topk_ids, (int)n, E, table, rank, dev_err);
     const unsigned grid = (unsigned)((T + kQpWaves - 1) / kQpWaves);
 #define QP_LAUNCH(C, B)                                                                          \
     quantize_permute_kernel<C, B><<<grid, kQpThreads, 0, s>>>(x, T, (int)H, topk_ids, (int)k,     \
-        (int)E, table, pchunks, codes, bscales, rscales, expert_offsets, row_to_tk, tk_to_row)
+        (int)E, table, rank, pchunks, codes, bscales, rscales, expert_offsets, row_to_tk,         \
+        tk_to_row)
     // rows of 1024, 2048 or 4096 elements: contiguous lanes; other lengths: strided lanes
     if (H == 1024) QP_LAUNCH(2, 1);
     else if (H == 2048) QP_LAUNCH(4, 2);
@@ -938,6 +1030,28 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
       }
     }
 #undef QP_LAUNCH
+  } else if (T > 0 && (int64_t)pchunks * E <= kMaxPlanTable && n <= INT32_MAX / 2 && H <= 4096) {
+    // long routing lists: ranks, one workgroup for the first rows, then rows +
+    // quantise + scatter with independent wavefronts
+    int32_t* rank = table + (int64_t)pchunks * E;
+    route_rank_kernel<<<pchunks, kPlanThreads, 0, s>>>(topk_ids, (int)n, E, table, rank, dev_err);
+    route_scan_kernel<<<1, kPlanThreads, 0, s>>>(table, pchunks, E, expert_offsets);
+    const unsigned grid = (unsigned)((T + kQrWaves - 1) / kQrWaves);
+#define QR_LAUNCH(C, B)                                                                          \
+    quantize_permute_rows_kernel<C, B><<<grid, kQrWaves * 64, 0, s>>>(x, T, (int)H, topk_ids,     \
+        (int)k, (int)E, table, rank, codes, bscales, rscales, row_to_tk, tk_to_row)
+    if (H == 1024) QR_LAUNCH(2, 1);
+    else if (H == 2048) QR_LAUNCH(4, 2);
+    else if (H == 4096) QR_LAUNCH(8, 4);
+    else {
+      switch (nch_for(H)) {
+        case 1: QR_LAUNCH(1, 0); break;
+        case 2: QR_LAUNCH(2, 0); break;
+        case 4: QR_LAUNCH(4, 0); break;
+        default: QR_LAUNCH(8, 0); break;
+      }
+    }
+#undef QR_LAUNCH
   } else {
     // long routing lists or long rows: plan over chunks of 1024 entries in many
     // workgroups (the last to arrive scans), then rank + quantise + scatter

@@ -114,8 +114,9 @@ def test_quantize_permute_full_config():
                                           (2000, 32, 3, "zipf"),        # groups of 24 entries straddle 4096-entry chunks
                                           (1700, 64, 5, "softmax"),     # ditto, 3 chunks
                                           (600, 1024, 8, "uniform"),    # 2 chunks x 1024 experts in the count table
-                                          (40000, 128, 8, "zipf"),      # 320k entries: many-workgroup plan
-                                          (3000, 1024, 32, "uniform")]) # 96k entries x 1024 experts: many-workgroup plan
+                                          (40000, 128, 8, "zipf"),      # 79 chunks: first rows by one workgroup, 8 threads per expert
+                                          (60000, 100, 6, "zipf"),      # 88 chunks, 10 scan threads per expert (1000 of 1024)
+                                          (3000, 1024, 32, "uniform")]) # 24 chunks x 1024 experts: one scan thread per expert
 def test_quantize_permute_ragged(T, E, k, kind):
     x = W.activations(T, 64 if T > 10000 else 256, config=9, tensor=T)
     ids, _ = W.make_routing(kind, T, E, k, config=9)
