@@ -131,7 +131,7 @@ NVFP4MOE_API int nvfp4_quantize_rows_tiled(const uint16_t* x, int64_t rows, int6
  * one workspace must be ordered (same stream, or synchronised): overlapping
  * calls on one workspace race.
  * Requires 1 <= k <= min(E, NVFP4MOE_MAX_TOPK), 1 <= E <= NVFP4MOE_MAX_EXPERTS,
- * H % 16 == 0, H <= NVFP4MOE_MAX_K.  k = 1, E = 1 with ids all 0 is a plain
+ * H % 16 == 0, H <= NVFP4MOE_MAX_K, T * k <= INT32_MAX / 2.  k = 1, E = 1 with ids all 0 is a plain
  * per-token quantisation (dense projections).
  */
 NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,

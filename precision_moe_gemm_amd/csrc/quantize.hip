@@ -18,15 +18,11 @@
 #include "common.h"
 
 #include <algorithm>
-#include <atomic>
-#include <random>
 
 namespace nvfp4moe {
 
 constexpr int kRowsPerBlock = 4;           // wavefronts (rows) per 256-thread workgroup
 constexpr int kChunk = 512;                // elements per wavefront per 16-byte-per-lane load
-constexpr int kRouteChunk = 1024;          // routing entries per route workgroup
-constexpr int kRouteThreads = 256;
 
 // ------------------------------------------------------------------ row quantiser
 template <int NCH>
@@ -358,190 +354,6 @@ __global__ __launch_bounds__(256) void quantize_rows_tiled_kernel(
   store_row_tiled<NCH>(o, sw, K, row, G, codes, bscales, rscales);
 }
 
-// ------------------------------------------------------------------ many-workgroup route plan
-// Plan: workgroup c counts chunk c (1024 routing entries) per expert and
-// publishes the counts; the last workgroup to arrive scans them over chunks
-// and experts and writes, in place,
-//   base[c][e] = offsets[e] + (entries of e in chunks before c)
-// and the offsets.  No workgroup waits for another.
-// The arrival counter is a 64-bit word (call tag << 32 | arrivals).  Every
-// call gets a fresh tag from the host, and the first arrival of a call finds
-// another tag and starts the count at 1, so the workspace needs no clearing
-// between calls or before its first use.
-constexpr int kPlanArrivalBytes = 256;               // workspace head: the arrival counter
-
-__device__ __forceinline__ uint32_t tagged_arrival(unsigned long long* ctr, uint32_t tag) {
-  unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  unsigned long long nv;
-  do {
-    nv = ((uint32_t)(old >> 32) == tag) ? old + 1ull : (((unsigned long long)tag << 32) | 1ull);
-  } while (!__hip_atomic_compare_exchange_weak(ctr, &old, nv, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT));
-  return (uint32_t)nv;
-}
-
-__global__ __launch_bounds__(kRouteThreads) void route_plan_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int E, int nchunks,
-    unsigned long long* __restrict__ arrivals, uint32_t tag, int32_t* __restrict__ table,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ dev_err) {
-  __shared__ int32_t h[NVFP4MOE_MAX_EXPERTS];
-  __shared__ uint32_t ticket;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) h[e] = 0;
-  __syncthreads();
-  const int64_t base0 = (int64_t)blockIdx.x * kRouteChunk;
-  int ev[kRouteChunk / kRouteThreads];
-#pragma unroll
-  for (int u = 0; u < kRouteChunk / kRouteThreads; ++u) {
-    const int64_t idx = base0 + u * kRouteThreads + threadIdx.x;
-    ev[u] = idx < n ? ids[idx] : 0;
-  }
-  bool bad = false;
-#pragma unroll
-  for (int u = 0; u < kRouteChunk / kRouteThreads; ++u) {
-    const int64_t idx = base0 + u * kRouteThreads + threadIdx.x;
-    if (idx < n) {
-      if (ev[u] >= 0 && ev[u] < E) atomicAdd(&h[ev[u]], 1);
-      else bad = true;
-    }
-  }
-  if (bad && dev_err) atomicOr(dev_err, NVFP4_DEVERR_BAD_EXPERT);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) table[(int64_t)blockIdx.x * E + e] = h[e];
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) ticket = tagged_arrival(arrivals, tag);
-  __syncthreads();
-  if (ticket != (uint32_t)nchunks) return;
-  // last workgroup: every chunk's counts are published
-  __threadfence();
-  __shared__ int32_t tot[NVFP4MOE_MAX_EXPERTS];
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
-    int acc = 0;
-    for (int c0 = 0; c0 < nchunks; c0 += 16) {
-      int v[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-        v[u] = (c0 + u < nchunks)
-            ? __hip_atomic_load(&table[(int64_t)(c0 + u) * E + e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-            : 0;
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (c0 + u < nchunks) {
-          table[(int64_t)(c0 + u) * E + e] = acc;
-          acc += v[u];
-        }
-      }
-    }
-    tot[e] = acc;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    int carry = 0;
-    for (int e0 = 0; e0 < E; e0 += kWave) {
-      const int e = e0 + lane;
-      const int v = e < E ? tot[e] : 0;
-      int incl = v;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int y = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += y;
-      }
-      if (e < E) {
-        tot[e] = carry + incl - v;
-        offsets[e] = carry + incl - v;
-      }
-      carry += __shfl(incl, kWave - 1, kWave);
-    }
-    if (lane == 0) offsets[E] = carry;
-  }
-  __syncthreads();
-  for (int64_t i = threadIdx.x; i < (int64_t)nchunks * E; i += kRouteThreads) table[i] += tot[i % E];
-}
-
-// Rank + quantise + scatter: one wavefront per token, 4 tokens per workgroup,
-// i.e. the 4k consecutive routing entries [4kw, 4kw + 4k).  An entry's row is
-// base[chunk][e] + (earlier entries of e in its chunk): the workgroup counts,
-// per expert, the entries between the start of its first entry's chunk and
-// its first entry, then ranks its own entries in order with ballot matching
-// on (chunk parity, expert) - its entries span at most two chunks.
-template <int NCH>
-__global__ __launch_bounds__(256) void quantize_route_kernel(
-    const uint16_t* __restrict__ x, int64_t T, int K, const int32_t* __restrict__ ids, int k, int E,
-    const int32_t* __restrict__ base, uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales,
-    float* __restrict__ rscales, int32_t* __restrict__ row_to_tk, int32_t* __restrict__ tk_to_row) {
-  // running counts per expert: [0] = first chunk (starting with the entries
-  // before the group), [1] = the next chunk (starting at zero)
-  __shared__ int32_t pre[2][NVFP4MOE_MAX_EXPERTS];
-  __shared__ int32_t rows[kRowsPerBlock * NVFP4MOE_MAX_TOPK];
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + wave;
-  // the token's activations first; it is quantised (in registers) while the
-  // routing loads of the group are in flight
-  RowCodes<NCH> o;
-  uint32_t sw[(NCH + 7) / 8];
-  if (t < T) {
-    uint4 raw[NCH];
-    load_bf16_raw<NCH>(x + t * (int64_t)K, K, raw);
-    float v[NCH][8];
-    unpack_bf16<NCH>(raw, v);
-    quantize_lane_row<NCH>(v, o);
-    pack_scales<NCH>(o, sw);
-  }
-
-  const int64_t n = T * (int64_t)k;
-  const int64_t e0 = (int64_t)blockIdx.x * kRowsPerBlock * k;          // first entry of the group
-  const int64_t e1 = min(e0 + (int64_t)kRowsPerBlock * k, n);          // one past the last
-  const int64_t cs = (e0 >> 10) << 10;                                 // start of e0's chunk
-  const int64_t second = cs + 1024;                                    // start of the next chunk
-  for (int e = threadIdx.x; e < E; e += 256) { pre[0][e] = 0; pre[1][e] = 0; }
-  __syncthreads();
-  for (int64_t i = cs + threadIdx.x; i < e0; i += 256) {
-    const int e = ids[i];
-    if (e >= 0 && e < E) atomicAdd(&pre[0][e], 1);
-  }
-  __syncthreads();
-  if (wave == 0) {
-    // the group's entries in order, 64 at a time (4k <= 128 entries, at most
-    // two chunks): equal (chunk, expert) pairs are found with ballots
-    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    for (int64_t i0 = e0; i0 < e1; i0 += kWave) {
-      const int64_t idx = i0 + lane;
-      const int e = idx < e1 ? ids[idx] : -1;
-      const bool valid = idx < e1 && e >= 0 && e < E;
-      const int part = idx >= second ? 1 : 0;
-      uint64_t peers = __ballot(valid);
-      const uint64_t pb = __ballot(valid && part);
-      peers &= part ? pb : ~pb;
-      for (int b = 0; b < nbits; ++b) {
-        const bool bit = valid && ((e >> b) & 1);
-        const uint64_t bb = __ballot(bit);
-        peers &= bit ? bb : ~bb;
-      }
-      const int r = __popcll(peers & lt_mask);
-      int row = -1;
-      if (valid) {
-        const int before = pre[part][e];
-        row = base[(idx >> 10) * E + e] + before + r;
-        if (r == 0) pre[part][e] = before + __popcll(peers);
-      }
-      if (idx < e1) {
-        tk_to_row[idx] = row;
-        rows[idx - e0] = row;
-        if (valid) row_to_tk[row] = (int32_t)idx;
-      }
-    }
-  }
-  __syncthreads();
-  if (t >= T) return;
-  const int my_row = lane < k ? rows[wave * k + lane] : -1;
-  for (int slot = 0; slot < k; ++slot) {
-    const int row = __shfl(my_row, slot, kWave);
-    if (row >= 0) store_row<NCH>(o, sw, K, row, codes, bscales, rscales);
-  }
-}
-
 // Route + permute + quantise in two launches.
 //
 // The rank pass: workgroup c (16 wavefronts) takes chunk c of 4096 routing
@@ -738,11 +550,10 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
 }
 
 // Long routing lists (a count table too large for every workgroup of the
-// main pass to scan): the ranks as above, then one workgroup turns the table
-// into first rows,
+// main pass to scan), long rows, or no tokens: the ranks as above, then one
+// workgroup turns the table into first rows,
 //   base[c][e] = offsets[e] + (entries of e in chunks before c),
 // in place and writes the offsets; the main pass then needs no scan at all.
-constexpr int64_t kMaxPlanTable = 1 << 20;   // chunks x experts (4 MiB of table)
 
 __global__ __launch_bounds__(kPlanThreads) void route_scan_kernel(
     int32_t* __restrict__ table, int nchunks, int E, int32_t* __restrict__ offsets) {
@@ -904,19 +715,6 @@ inline int nch_for(int64_t K) {
     default: KERNEL<16><<<GRID, 256, 0, STREAM>>>(__VA_ARGS__); break;                  \
   }
 
-// Tag of the next route-plan launch: distinct for 2^32 consecutive calls of
-// the process, starting from a random value so that a workspace's initial
-// contents are very unlikely to hold the first tag.
-inline uint32_t next_call_tag() {
-  static std::atomic<uint32_t> tag{std::random_device{}()};
-  return tag.fetch_add(1u, std::memory_order_relaxed);
-}
-
-inline int64_t route_chunks(int64_t T, int32_t k) {
-  const int64_t n = T * (int64_t)k;
-  return n > 0 ? (n + kRouteChunk - 1) / kRouteChunk : 1;
-}
-
 }  // namespace nvfp4moe
 
 using namespace nvfp4moe;
@@ -940,11 +738,9 @@ NVFP4MOE_API int nvfp4moe_abi_version(void) { return NVFP4MOE_ABI_VERSION; }
 
 NVFP4MOE_API size_t nvfp4moe_permute_workspace_size(int64_t T, int32_t k, int32_t E) {
   if (T < 0 || k <= 0 || E <= 0) return 0;
-  // the larger of the two plans: (chunk, expert) counts of 1024-entry chunks,
-  // or of 4096-entry chunks plus a rank per routing entry
+  // the (chunk, expert) count table and a rank per routing entry
   const int64_t n = T * (int64_t)k;
-  const int64_t ints = std::max<int64_t>(route_chunks(T, k) * E, (int64_t)plan_chunks(n) * E + n);
-  const size_t bytes = kPlanArrivalBytes + (size_t)ints * sizeof(int32_t);
+  const size_t bytes = ((size_t)plan_chunks(n) * (size_t)E + (size_t)n) * sizeof(int32_t);
   return (bytes + 255) & ~(size_t)255;
 }
 
@@ -993,7 +789,8 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
   if (T < 0 || H <= 0 || H % 16 != 0 || H > NVFP4MOE_MAX_K) return NVFP4_ERR_SHAPE;
   if (E < 1 || E > NVFP4MOE_MAX_EXPERTS || k < 1 || k > E || k > NVFP4MOE_MAX_TOPK)
     return NVFP4_ERR_SHAPE;
-  if (T * (int64_t)k > INT32_MAX) return NVFP4_ERR_SHAPE;
+  // entry indices, plus a chunk's worth past the last, stay in int
+  if (T * (int64_t)k > INT32_MAX / 2) return NVFP4_ERR_SHAPE;
   if (!expert_offsets || !workspace) return NVFP4_ERR_NULL;
   if (T > 0 && (!x || !topk_ids || !codes || !bscales || !rscales || !row_to_tk || !tk_to_row))
     return NVFP4_ERR_NULL;
@@ -1003,15 +800,14 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
   if (workspace_bytes < nvfp4moe_permute_workspace_size(T, k, E)) return NVFP4_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t n = T * (int64_t)k;
-  const int nchunks = (int)route_chunks(T, k);
-  unsigned long long* arrivals = static_cast<unsigned long long*>(workspace);
-  int32_t* table = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + kPlanArrivalBytes);
   const int pchunks = plan_chunks(n);
-  if (T > 0 && (int64_t)pchunks * E <= kCountTable && n <= INT32_MAX / 2 && H <= 4096) {
-    // rank every entry within its chunk and expert and count per (chunk,
-    // expert); then offsets + rows + quantise + scatter
-    int32_t* rank = table + (int64_t)pchunks * E;
-    route_rank_kernel<<<pchunks, kPlanThreads, 0, s>>>(topk_ids, (int)n, E, table, rank, dev_err);
+  int32_t* table = static_cast<int32_t*>(workspace);        // [pchunks][E]
+  int32_t* rank = table + (int64_t)pchunks * E;              // [n]
+  // rank every entry within its chunk and expert, and count per (chunk, expert)
+  route_rank_kernel<<<pchunks, kPlanThreads, 0, s>>>(topk_ids, (int)n, E, table, rank, dev_err);
+  if (T > 0 && (int64_t)pchunks * E <= kCountTable && H <= 4096) {
+    // offsets + first rows from the table in every workgroup, then rows +
+    // quantise + scatter
     const unsigned grid = (unsigned)((T + kQpWaves - 1) / kQpWaves);
 #define QP_LAUNCH(C, B)                                                                          \
     quantize_permute_kernel<C, B><<<grid, kQpThreads, 0, s>>>(x, T, (int)H, topk_ids, (int)k,     \
@@ -1030,12 +826,13 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
       }
     }
 #undef QP_LAUNCH
-  } else if (T > 0 && (int64_t)pchunks * E <= kMaxPlanTable && n <= INT32_MAX / 2 && H <= 4096) {
-    // long routing lists: ranks, one workgroup for the first rows, then rows +
-    // quantise + scatter with independent wavefronts
-    int32_t* rank = table + (int64_t)pchunks * E;
-    route_rank_kernel<<<pchunks, kPlanThreads, 0, s>>>(topk_ids, (int)n, E, table, rank, dev_err);
-    route_scan_kernel<<<1, kPlanThreads, 0, s>>>(table, pchunks, E, expert_offsets);
+    return launch_status();
+  }
+  // long routing lists, long rows, or no tokens: one workgroup turns the table
+  // into first rows and writes the offsets; then rows + quantise + scatter
+  // with independent wavefronts
+  route_scan_kernel<<<1, kPlanThreads, 0, s>>>(table, pchunks, E, expert_offsets);
+  if (T > 0) {
     const unsigned grid = (unsigned)((T + kQrWaves - 1) / kQrWaves);
 #define QR_LAUNCH(C, B)                                                                          \
     quantize_permute_rows_kernel<C, B><<<grid, kQrWaves * 64, 0, s>>>(x, T, (int)H, topk_ids,     \
@@ -1048,21 +845,11 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
         case 1: QR_LAUNCH(1, 0); break;
         case 2: QR_LAUNCH(2, 0); break;
         case 4: QR_LAUNCH(4, 0); break;
-        default: QR_LAUNCH(8, 0); break;
+        case 8: QR_LAUNCH(8, 0); break;
+        default: QR_LAUNCH(16, 0); break;
       }
     }
 #undef QR_LAUNCH
-  } else {
-    // long routing lists or long rows: plan over chunks of 1024 entries in many
-    // workgroups (the last to arrive scans), then rank + quantise + scatter
-    route_plan_kernel<<<nchunks, kRouteThreads, 0, s>>>(topk_ids, n, E, nchunks, arrivals,
-                                                        next_call_tag(), table, expert_offsets,
-                                                        dev_err);
-    if (T > 0) {
-      const dim3 grid((unsigned)((T + kRowsPerBlock - 1) / kRowsPerBlock));
-      NVFP4_DISPATCH_NCH(H, quantize_route_kernel, grid, s, x, T, (int)H, topk_ids, (int)k, (int)E,
-                         table, codes, bscales, rscales, row_to_tk, tk_to_row);
-    }
   }
   return launch_status();
 }

@@ -43,7 +43,8 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.nvfp4moe_permute_workspace_size(4096, 8, 128) >= 32 * 128 * 4
+    # a (chunk of 4096 entries, expert) count table and one rank per routing entry
+    assert lib.nvfp4moe_permute_workspace_size(4096, 8, 128) >= (8 * 128 + 32768) * 4
     assert lib.nvfp4moe_permute_workspace_size(0, 8, 128) >= 128 * 4
     assert lib.nvfp4moe_permute_workspace_size(-1, 8, 128) == 0
 
@@ -76,6 +77,7 @@ def test_quantize_permute_host_checks(lib):
     assert f(*args(ws=None)) == ERR_NULL
     assert f(*args(wsb=ws - 1)) == ERR_WORKSPACE
     assert f(*args(x=FAKE + 8)) == ERR_ALIGN
+    assert f(*args(T=1 << 27, k=8, wsb=1 << 40)) == ERR_SHAPE   # T k above INT32_MAX / 2
 
 
 def test_gemm_host_checks(lib):

@@ -132,7 +132,7 @@ def test_quantize_permute_row_lengths(H):
 
 
 def test_quantize_permute_long_rows():
-    """H > 4096 takes the many-workgroup plan and the 1-token-per-wavefront pass."""
+    """H > 4096 takes the first-row scan and the independent-wavefront pass (16 chunks of 512 per lane)."""
     x = W.activations(50, 8192, config=9, tensor=3)
     ids, _ = W.make_routing("uniform", 50, 16, 4, config=9)
     _check_permute(x, ids, 16, "H=8192")
