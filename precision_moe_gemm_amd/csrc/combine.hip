@@ -70,17 +70,16 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(
   const float* grow = gu + r * (int64_t)(2 * I);
   const float* drow = dh + r * (int64_t)I;
   uint16_t* orow = dgu + r * (int64_t)(2 * I);
-  for (int base = lane_id() * 8; base < I; base += kWave * 8) {
-    float gs[8], us[8], ds[8];
+  // 4 elements per lane per step (256 per wavefront), so that a row of any
+  // multiple of 256 keeps every lane busy in the float64 work
+  for (int base = lane_id() * 4; base < I; base += kWave * 4) {
+    float gs[4], us[4], ds[4];
     *reinterpret_cast<float4*>(gs) = *reinterpret_cast<const float4*>(grow + base);
-    *reinterpret_cast<float4*>(gs + 4) = *reinterpret_cast<const float4*>(grow + base + 4);
     *reinterpret_cast<float4*>(us) = *reinterpret_cast<const float4*>(grow + I + base);
-    *reinterpret_cast<float4*>(us + 4) = *reinterpret_cast<const float4*>(grow + I + base + 4);
     *reinterpret_cast<float4*>(ds) = *reinterpret_cast<const float4*>(drow + base);
-    *reinterpret_cast<float4*>(ds + 4) = *reinterpret_cast<const float4*>(drow + base + 4);
-    uint32_t og[4], ou[4];
+    uint32_t og[2], ou[2];
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
+    for (int j = 0; j < 4; j += 2) {
       uint32_t bg[2], bu[2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -97,8 +96,8 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(
       og[j / 2] = bg[0] | (bg[1] << 16);
       ou[j / 2] = bu[0] | (bu[1] << 16);
     }
-    *reinterpret_cast<uint4*>(orow + base) = make_uint4(og[0], og[1], og[2], og[3]);
-    *reinterpret_cast<uint4*>(orow + I + base) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+    *reinterpret_cast<uint2*>(orow + base) = make_uint2(og[0], og[1]);
+    *reinterpret_cast<uint2*>(orow + I + base) = make_uint2(ou[0], ou[1]);
   }
 }
 

@@ -665,9 +665,46 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
   const int lane = lane_id();
   const float* grow = gu + r * (int64_t)(2 * I);
   const float w = topk_w ? topk_w[row_to_tk[r]] : 1.0f;
+  // SwiGLU of one element: float64, in the order of the definition, rounded once
+  auto swiglu = [&](float gf, float uf) __attribute__((always_inline)) -> float {
+    const double g = gf;
+    const double e = exp(-g);
+    double hv = (g / (1.0 + e)) * (double)uf;
+    if (topk_w) hv = hv * (double)w;
+    return (float)hv;
+  };
+  // The quantiser's layout gives lane l elements c*512 + 8l .. +7; a last chunk
+  // of at most 256 elements would leave half the lanes idle in the float64
+  // work, so there lane l computes elements 4l .. 4l+3 and the values move to
+  // their lanes by shuffles (same arithmetic, same results).
+  const int tail = I - (NCH - 1) * kChunk;             // elements in the last chunk
+  const bool split_tail = tail <= kChunk / 2;
   float h[NCH][8];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
+    if (c == NCH - 1 && split_tail) {
+      const int b4 = c * kChunk + lane * 4;
+      float hb[4] = {0.f, 0.f, 0.f, 0.f};
+      if (lane * 4 < tail) {
+        const float4 g4 = *reinterpret_cast<const float4*>(grow + b4);
+        const float4 u4 = *reinterpret_cast<const float4*>(grow + I + b4);
+        hb[0] = swiglu(g4.x, u4.x);
+        hb[1] = swiglu(g4.y, u4.y);
+        hb[2] = swiglu(g4.z, u4.z);
+        hb[3] = swiglu(g4.w, u4.w);
+        if (h_out)
+          *reinterpret_cast<float4*>(h_out + r * (int64_t)I + b4) = make_float4(hb[0], hb[1], hb[2], hb[3]);
+      }
+      const bool mine = lane * 8 < tail;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float lo = __shfl(hb[j], 2 * lane, kWave);       // from lane 2l: elements 8l .. 8l+3
+        const float hi = __shfl(hb[j], 2 * lane + 1, kWave);   // from lane 2l+1: 8l+4 .. 8l+7
+        h[c][j] = mine ? lo : 0.0f;
+        h[c][4 + j] = mine ? hi : 0.0f;
+      }
+      continue;
+    }
     const int base = c * kChunk + lane * 8;
     if (base < I) {
       const float4 g0 = *reinterpret_cast<const float4*>(grow + base);
@@ -677,13 +714,7 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
       const float gs[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
       const float us[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const double g = gs[j];
-        const double e = exp(-g);
-        double hv = (g / (1.0 + e)) * (double)us[j];
-        if (topk_w) hv = hv * (double)w;
-        h[c][j] = (float)hv;
-      }
+      for (int j = 0; j < 8; ++j) h[c][j] = swiglu(gs[j], us[j]);
       if (h_out) {
         float* hrow = h_out + r * (int64_t)I + base;
         *reinterpret_cast<float4*>(hrow) = make_float4(h[c][0], h[c][1], h[c][2], h[c][3]);
