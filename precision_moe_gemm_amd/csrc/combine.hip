@@ -21,21 +21,36 @@ __global__ __launch_bounds__(256) void unpermute_combine_kernel(
   const int lane = lane_id();
   const int my_row = lane < k ? tk_to_row[t * k + lane] : -1;
   const float my_w = (lane < k && topk_w) ? topk_w[t * k + lane] : 1.0f;
-  // The loop is wave-uniform (every lane runs every slot) because the slot's
-  // row and weight are fetched with cross-lane shuffles.
+  // The loops are wave-uniform (every lane runs every slot) because the slot's
+  // row and weight are fetched with cross-lane shuffles.  Slots go in groups
+  // of 8 whose loads are all issued before the first is added, so that 8 KiB
+  // per wavefront are in flight; the sum still runs in slot order.
   for (int c0 = 0; c0 < H; c0 += kWave * 4) {
     const int base = c0 + lane * 4;
     const bool inside = base < H;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     bool started = false;
-    for (int s = 0; s < k; ++s) {
-      const int row = __shfl(my_row, s, kWave);
-      const float w = __shfl(my_w, s, kWave);
-      if (row < 0 || !inside) continue;
-      float4 v = *reinterpret_cast<const float4*>(d + (int64_t)row * H + base);
-      if (topk_w) { v.x = w * v.x; v.y = w * v.y; v.z = w * v.z; v.w = w * v.w; }
-      if (started) { acc.x = acc.x + v.x; acc.y = acc.y + v.y; acc.z = acc.z + v.z; acc.w = acc.w + v.w; }
-      else { acc = v; started = true; }
+    for (int s0 = 0; s0 < k; s0 += 8) {
+      float4 v[8];
+      float wv[8];
+      bool ok[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int sl = s0 + u;                       // < 40: a lane index
+        const int row = __shfl(my_row, sl, kWave);
+        wv[u] = __shfl(my_w, sl, kWave);
+        ok[u] = sl < k && row >= 0 && inside;
+        v[u] = ok[u] ? *reinterpret_cast<const float4*>(d + (int64_t)row * H + base)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (!ok[u]) continue;
+        float4 x = v[u];
+        if (topk_w) { x.x = wv[u] * x.x; x.y = wv[u] * x.y; x.z = wv[u] * x.z; x.w = wv[u] * x.w; }
+        if (started) { acc.x = acc.x + x.x; acc.y = acc.y + x.y; acc.z = acc.z + x.z; acc.w = acc.w + x.w; }
+        else { acc = x; started = true; }
+      }
     }
     if (!inside) continue;
     uint2 o;
