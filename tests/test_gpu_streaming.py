@@ -182,3 +182,33 @@ def test_bf16_grouped_gemm_gather(T, E, k, K, N, kind):
         rows = np.arange(Rv)
     ref, bound = og.bf16_grouped_gemm_ref(a_perm, off, of.bf16_to_f32(w), trans_w=False, rows=rows)
     print("  err/bound", assert_within(c[rows], ref, bound, "gather gemm"))
+
+
+@pytest.mark.parametrize("N", [16, 272])
+def test_bf16_grouped_gemm_narrow_and_ragged_columns(N):
+    """N = 16 (one 16-column group) and N = 272 (a ragged last 256-column tile)."""
+    print(f"[bf16 gemm] N={N}", flush=True)
+    T, E, k, K = 300, 8, 2, 64
+    ids, tw, off, r2t, t2r = _routing(T, E, k, "zipf", 66)
+    a = W.gaussian_bf16((T * k, K), 1.0, 66, 40)
+    w = W.gaussian_bf16((E, K, N), 0.02, 66, 41)
+    c = host(pmg.bf16_grouped_gemm(bf16_dev(a), dev(off), bf16_dev(w), pmg.W_KN))
+    ref, bound = og.bf16_grouped_gemm_ref(of.bf16_to_f32(a), off, of.bf16_to_f32(w), trans_w=False)
+    Rv = int(off[-1])
+    print("  err/bound", assert_within(c[:Rv], ref, bound, "bf16 gemm"))
+
+
+def test_bf16_grouped_gemm_gather_clamps_bad_map_entries():
+    """Map entries outside [0, T k) read a row clamped into [0, T): a wrong row, never outside a."""
+    print("[bf16 gemm gather] bad map entries", flush=True)
+    T, E, k, K, N = 64, 4, 2, 64, 48
+    ids, tw, off, r2t, t2r = _routing(T, E, k, "uniform", 67)
+    bad = r2t.copy()
+    bad[3], bad[10], bad[20] = 10 ** 9, -5, T * k + 7
+    x = W.gaussian_bf16((T, K), 1.0, 67, 42)
+    w = W.gaussian_bf16((E, K, N), 0.02, 67, 43)
+    c = host(pmg.bf16_grouped_gemm_gather(bf16_dev(x), dev(bad), k, dev(off), bf16_dev(w)))
+    Rv = int(off[-1])
+    tok = np.minimum(np.maximum(bad[:Rv].astype(np.int64), 0) // k, T - 1)
+    ref, bound = og.bf16_grouped_gemm_ref(of.bf16_to_f32(x)[tok], off, of.bf16_to_f32(w), trans_w=False)
+    print("  err/bound", assert_within(c[:Rv], ref, bound, "gather gemm (clamped)"))
