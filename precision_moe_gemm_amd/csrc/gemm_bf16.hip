@@ -27,7 +27,7 @@
 //     first operand, which leaves 4 consecutive output columns in each lane for
 //     16-byte stores.  The activation tile's 16-byte chunks are XOR-swizzled by
 //     row (conflict-free fragment reads); a [K][N] weight tile keeps its rows
-//     in LDS (16-byte chunks XOR-swizzled by row) and each fragment is read
+//     in LDS (16-byte chunks XOR-swizzled by row, wswz) and each fragment is read
 //     with two transposing LDS reads (ds_read_b64_tr_b16);
 //   * a tile's stores are issued after the first barrier of the next tile, so
 //     a wait for loads never has to cover them;
@@ -79,6 +79,13 @@ struct __align__(16) Smem {
 // physical 16-byte chunk of logical chunk c (0..3) of row r: rows r..r+15 of
 // one fragment read land in 16 distinct 16-byte bank groups
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// [K][N] weight tile: physical 16-byte chunk p of row k holds logical chunk
+// p ^ wswz(k).  A transposing read covers rows k0..k0+3 in each group of 16
+// lanes, and one LDS cycle serves two groups, whose rows are 8 apart: the
+// 2 (k % 4) term spreads the 4 rows over distinct banks, the 8 ((k / 8) % 2)
+// term moves the second group's rows to the other half of the banks.
+__device__ __forceinline__ int wswz(int k) { return (2 * (k & 3)) | (8 * ((k >> 3) & 1)); }
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
@@ -249,7 +256,7 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
       if (KN) {
         // physical chunk lane%32 of row k holds logical chunk (lane%32) ^ 2(k%4)
         const int k = 2 * q + (lane >> 5);
-        const int n = min(t.n0 + 8 * ((lane & 31) ^ (2 * (k & 3))), N - 8);
+        const int n = min(t.n0 + 8 * ((lane & 31) ^ wswz(k)), N - 8);
         off_w[u] = (((uint32_t)t.e * K + k) * N + n) * 2u;
       } else {
         const int r = 16 * q + (lane >> 2);
@@ -304,7 +311,7 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int k = 8 * g + 4 * hh + (l16 >> 2);
-          const int pc = (col >> 3) ^ (2 * (k & 3));
+          const int pc = (col >> 3) ^ wswz(k);
           v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_v4i16*)(S.w + k * (BN * 2) + pc * 16 + ((col >> 2) & 1) * 8));
         }
