@@ -23,7 +23,11 @@
 //   * FP4 codes (32 B per row per K-step) and E4M3 scales (4 B per row) of
 //     both operands go from global memory straight into LDS
 //     (global_load_lds) in a 3-stage ring: the loads of K-step g+3 are issued
-//     when K-step g starts, two full K-steps before they are read.
+//     when K-step g starts, two full K-steps before they are read.  With
+//     K-tiled weights every wavefront issues the same three loads per K-step
+//     from per-tile offsets (the weight block scales of a K-step are then
+//     contiguous, 16 bytes = 4 rows per lane), so the issue has no branches
+//     beyond one on the load width.
 //   * The activation tile is shared by the 8 wavefronts, so it is decoded once
 //     per K-step, cooperatively, into an FP16 tile in LDS (128 B rows, 16-byte
 //     chunks XOR-swizzled by row); each wavefront decodes only its own weight
@@ -142,6 +146,15 @@ __device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t voff, con
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
                :: "s"(m), "v"(voff), "s"(base) : "memory", "m0");
 }
+// the same with the LDS destination given as a wave-uniform LDS byte address
+__device__ __forceinline__ void lds_dma16_at(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4_at(const uint8_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds), "v"(voff), "s"(base) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ void wait_vmcnt(int n) {
@@ -174,13 +187,15 @@ __device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_star
   return t;
 }
 
+template <bool KT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_bscales,
     const float* __restrict__ a_rscales, const int32_t* __restrict__ offsets, int E,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_bscales,
-    const float* __restrict__ w_rscales, int N, int K, float* __restrict__ c, int w_tiled) {
+    const float* __restrict__ w_rscales, int N, int K, float* __restrict__ c) {
   __shared__ Smem sm;
+  constexpr bool w_tiled = KT;
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -226,8 +241,9 @@ void grouped_gemm_kernel(
 
   const uint32_t kb = (uint32_t)K / 2, ks = (uint32_t)K / 16;
   const int nk = K / BK;
-  // instructions q = wave + kWaves * u of each kind fall to this wavefront
-  const int n_loads = (kCI - wave + kWaves - 1) / kWaves + (kSI - wave + kWaves - 1) / kWaves;
+  // row-major weights: instructions q = wave + kWaves * u of each kind fall to
+  // this wavefront
+  const int n_loads = KT ? 3 : (kCI - wave + kWaves - 1) / kWaves + (kSI - wave + kWaves - 1) / kWaves;
 
   // ---------------------------------------------------------------- loads
   // Load cursor: the next K-step to load is (ltile, lk).  Each lane's sources
@@ -242,8 +258,41 @@ void grouped_gemm_kernel(
   // contiguous memory.
   const uint32_t wstep_c = w_tiled ? (uint32_t)N * kRowB : (uint32_t)kRowB;
   const uint32_t wstep_s = w_tiled ? (uint32_t)N * kScB : (uint32_t)kScB;
+  // K-tiled weights: three loads per wavefront and K-step.  Slots 0 and 1
+  // carry code rows q = w and q = w + 8 (32 rows each; q < 4 are activation
+  // rows, the rest weight rows); slot 2 carries code rows q = w + 16 (w < 4),
+  // the weight block scales of 256 rows (w = 4, 5: 16 bytes = 4 rows per lane)
+  // or the activation block scales of 64 rows (w = 6, 7: 4 bytes per lane).
+  // Per slot: the source operand, the per-lane offset of the tile (set per
+  // tile), the offset step per K-step and the LDS offset in a stage.
+  const uint8_t* src0 = wave < 4 ? a_codes : w_codes;
+  const uint8_t* src2 = wave < 4 ? w_codes : wave < 6 ? w_bscales : a_bscales;
+  const uint32_t step0 = wave < 4 ? (uint32_t)kRowB : (uint32_t)N * kRowB;
+  const uint32_t step1 = (uint32_t)N * kRowB;
+  const uint32_t step2 = wave < 4 ? (uint32_t)N * kRowB : wave < 6 ? (uint32_t)N * kScB : (uint32_t)kScB;
+  const uint32_t lds_st = (uint32_t)(uintptr_t)(lds_void*)&sm.st[0];
+  const uint32_t ldo0 = (uint32_t)wave * 1024u, ldo1 = (uint32_t)(wave + 8) * 1024u;
+  const uint32_t ldo2 = wave < 4 ? (uint32_t)(wave + 16) * 1024u
+                        : wave < 6 ? (uint32_t)offsetof(Stage, ws) + (uint32_t)(wave - 4) * 1024u
+                                   : (uint32_t)offsetof(Stage, as) + (uint32_t)(wave - 6) * 256u;
+  uint32_t vo0 = 0, vo1 = 0, vo2 = 0;
   auto set_load_tile = [&](int L) __attribute__((always_inline)) {
     const Tile t = tile_at(L, n_tiles, sm.tile_start, E, offsets);
+    if constexpr (KT) {
+      const int m_last = t.m0 + t.rows - 1;
+      const uint32_t half16 = (lane & 1) * 16;
+      const uint32_t wbase = (uint32_t)t.e * nk * N;
+      auto wrow = [&](int q) __attribute__((always_inline)) {
+        const uint32_t n = (uint32_t)min(t.n0 + 32 * (q - BM / 32) + (lane >> 1), N - 1);
+        return (wbase + n) * kRowB + half16;
+      };
+      vo0 = wave < 4 ? (uint32_t)min(t.m0 + 32 * wave + (lane >> 1), m_last) * kb + half16 : wrow(wave);
+      vo1 = wrow(wave + 8);
+      if (wave < 4) vo2 = wrow(wave + 16);
+      else if (wave < 6) vo2 = (wbase + (uint32_t)min(t.n0 + 256 * (wave - 4) + 4 * lane, N - 4)) * kScB;
+      else vo2 = (uint32_t)min(t.m0 + 64 * (wave - 6) + lane, m_last) * ks;
+      return;
+    }
     const int m_last = t.m0 + t.rows - 1;
     const int half = lane & 1;
 #pragma unroll
@@ -272,6 +321,19 @@ void grouped_gemm_kernel(
   // cursor; returns the number of load instructions this wavefront issued
   auto issue_loads = [&](Stage& S) __attribute__((always_inline)) -> int {
     if (lL >= end) return 0;
+    if constexpr (KT) {
+      const uint32_t ls = lds_st + (uint32_t)((uintptr_t)(lds_void*)&S - (uintptr_t)(lds_void*)&sm.st[0]);
+      lds_dma16_at(src0, (uint32_t)lk * step0 + vo0, ls + ldo0);
+      lds_dma16_at(w_codes, (uint32_t)lk * step1 + vo1, ls + ldo1);
+      if (wave < 6) lds_dma16_at(src2, (uint32_t)lk * step2 + vo2, ls + ldo2);
+      else lds_dma4_at(src2, (uint32_t)lk * step2 + vo2, ls + ldo2);
+      if (++lk == nk) {
+        lk = 0;
+        lL += step;
+        if (lL < end) set_load_tile(lL);
+      }
+      return 3;
+    }
     const uint32_t ka = (uint32_t)lk * kRowB, kss = (uint32_t)lk * kScB;
     const uint32_t kw = (uint32_t)lk * wstep_c, kws = (uint32_t)lk * wstep_s;
 #pragma unroll
@@ -398,18 +460,19 @@ void grouped_gemm_kernel(
   // Row scales of a tile for its epilogue, into one of two LDS buffers (tile
   // parity): issued at the top of the tile's last K-step, ahead of that step's
   // loads, so that waiting for the loads counted in n_last also waits for them.
+  // The row scales go in four loads: wavefronts 0 and 1 the activation rows
+  // (64 per load, 4 bytes per lane), 2 and 3 the weight rows (256 per load,
+  // 16 bytes = 4 rows per lane).
+  const uint32_t lds_rs = (uint32_t)(uintptr_t)(lds_void*)&sm.rs[0][0];
   auto issue_rscales = [&](const Tile& t, int rb) __attribute__((always_inline)) {
-    const uint8_t* dst = reinterpret_cast<const uint8_t*>(sm.rs[rb]);
-#pragma unroll
-    for (int u = 0; u < kSIW; ++u) {
-      const int q = wave + kWaves * u;   // 0,1 -> A rows, 2.. -> W rows
-      if (q < 2)
-        lds_dma4(reinterpret_cast<const uint8_t*>(a_rscales),
-                 (uint32_t)min(t.m0 + 64 * q + lane, t.m0 + t.rows - 1) * 4u, dst + q * 256);
-      else if (q < kSI)
-        lds_dma4(reinterpret_cast<const uint8_t*>(w_rscales),
-                 ((uint32_t)t.e * N + min(t.n0 + 64 * (q - 2) + lane, N - 1)) * 4u, dst + q * 256);
-    }
+    const uint32_t dst = lds_rs + (uint32_t)rb * (BM + BN) * 4u;
+    if (wave < 2)
+      lds_dma4_at(reinterpret_cast<const uint8_t*>(a_rscales),
+                  (uint32_t)min(t.m0 + 64 * wave + lane, t.m0 + t.rows - 1) * 4u, dst + wave * 256u);
+    else if (wave < 4)
+      lds_dma16_at(reinterpret_cast<const uint8_t*>(w_rscales),
+                   ((uint32_t)t.e * N + min(t.n0 + 256 * (wave - 2) + 4 * lane, N - 4)) * 4u,
+                   dst + BM * 4u + (wave - 2) * 1024u);
   };
 
   // epilogue: C = (acc * s_A[row]) * s_W[col].  Tile (i, j) of the lane holds
@@ -542,8 +605,13 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uin
   int64_t grid = max_tiles < 256 ? max_tiles : 256;
   if (grid >= 8) grid &= ~7ll;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  g5::grouped_gemm_kernel<<<(unsigned)grid, g5::kThreads, 0, s>>>(
-      a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales, (int)N,
-      (int)K, c, (int)(w_layout == NVFP4_W_KTILED));
+  if (w_layout == NVFP4_W_KTILED)
+    g5::grouped_gemm_kernel<true><<<(unsigned)grid, g5::kThreads, 0, s>>>(
+        a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales, (int)N,
+        (int)K, c);
+  else
+    g5::grouped_gemm_kernel<false><<<(unsigned)grid, g5::kThreads, 0, s>>>(
+        a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales, (int)N,
+        (int)K, c);
   return launch_status();
 }
