@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--routing", default="softmax", choices=["softmax", "uniform", "zipf"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-comparisons", action="store_true",
+                   help="skip the BF16 forward and NVFP4 input-gradient timings after the timed steps")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the oracle sample's CPU time")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only copy MIB MiB device to device 4 times (calibrates the HBM byte counters)")
@@ -258,9 +260,93 @@ def main():
     }
 
     result["practical_ceiling"] = practical_ceiling(gu_tf, per_op["quantize_permute"]["GBps"])
+    if not args.no_comparisons:
+        result["comparisons"] = comparisons(
+            dict(x=x, dy=dy, ids=ids, E=E, k=k, I=I, H=H, perm=perm, wgu=wgu, wd=wd, dgu=dgu, ws=ws),
+            gemm_flops, op_ms)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_bits, ids_np, wgu_bits, S, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def _time_op(fn, reps=10):
+    """Average µs of one launch of fn: 3 untimed, then reps timed on the launch stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        fn()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    st.record(stream)
+    for _ in range(reps):
+        fn()
+    en.record(stream)
+    torch.cuda.synchronize()
+    return st.elapsed_time(en) * 1e3 / reps
+
+
+def comparisons(t, gemm_flops, op_ms):
+    """The same layer at other precisions, timed after the timed steps (outside them):
+    the forward's expert GEMMs in BF16 (the precision NVFP4 replaces), and the
+    input gradient's GEMMs in NVFP4 (a lower-precision backward: the output
+    gradient quantised and permuted like the forward input, the SwiGLU gradient
+    quantised per row, the forward weights transposed and quantised along their
+    output dimension once, untimed)."""
+    import torch
+    import precision_moe_gemm_amd as pmg
+    x, dy, ids, E, k, I, H = t["x"], t["dy"], t["ids"], t["E"], t["k"], t["I"], t["H"]
+    perm, off = t["perm"], t["perm"]["expert_offsets"]
+    R = perm["row_to_tk"].numel()
+    dev = x.device
+    tf = lambda name, us: round(gemm_flops[name] / (us * 1e-6) / 1e12, 1)
+    out = {}
+    # BF16 forward: gate_up reads the token rows through the routing map, down a BF16 SwiGLU output
+    gu_bf = torch.empty(R, 2 * I, dtype=torch.float32, device=dev)
+    h16 = t["dgu"][:, :I].contiguous()
+    dn_bf = torch.empty(R, H, dtype=torch.float32, device=dev)
+    us_gu = _time_op(lambda: pmg.bf16_grouped_gemm_gather(x, perm["row_to_tk"], k, off, t["wgu"], pmg.W_NK,
+                                                          c=gu_bf))
+    us_dn = _time_op(lambda: pmg.bf16_grouped_gemm(h16, off, t["wd"], pmg.W_NK, c=dn_bf))
+    nv = (op_ms["gate_up_gemm"] + op_ms["down_gemm"]) * 1e3
+    out["bf16_forward"] = {
+        "gate_up_gemm": {"us": round(us_gu, 2), "TFLOPs": tf("gate_up_gemm", us_gu)},
+        "down_gemm": {"us": round(us_dn, 2), "TFLOPs": tf("down_gemm", us_dn)},
+        "nvfp4_gemms_speedup": round((us_gu + us_dn) / nv, 3)}
+    del gu_bf, dn_bf, h16
+    # NVFP4 input gradient
+    def transposed_nvfp4(w):     # [E, out, in] -> quantised [E, in, out] along out, K-tiled
+        wt = pmg.bf16_transpose(w)
+        c_, b_, s_ = pmg.nvfp4_quantize_rows_tiled(wt.view(-1, wt.shape[2]), wt.shape[1])
+        return c_, b_, s_.view(-1, wt.shape[1])
+    q_dt, q_gut = transposed_nvfp4(t["wd"]), transposed_nvfp4(t["wgu"])
+    torch.cuda.synchronize()
+    pdy = {"codes": torch.empty(R, H // 2, dtype=torch.uint8, device=dev),
+           "bscales": torch.empty(R, H // 16, dtype=torch.uint8, device=dev),
+           "rscales": torch.empty(R, dtype=torch.float32, device=dev),
+           "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+           "row_to_tk": torch.empty(R, dtype=torch.int32, device=dev),
+           "tk_to_row": torch.empty(R, dtype=torch.int32, device=dev)}
+    g = (torch.empty(R, I, dtype=torch.uint8, device=dev), torch.empty(R, I // 8, dtype=torch.uint8, device=dev),
+         torch.empty(R, dtype=torch.float32, device=dev))
+    dh = torch.empty(R, I, dtype=torch.float32, device=dev)
+    dxp = torch.empty(R, H, dtype=torch.float32, device=dev)
+    us_qp = _time_op(lambda: pmg.nvfp4_quantize_permute(dy, ids, E, workspace=t["ws"], out=pdy))
+    us_dd = _time_op(lambda: pmg.nvfp4_grouped_gemm(pdy["codes"], pdy["bscales"], pdy["rscales"],
+                                                    pdy["expert_offsets"], *q_dt, c=dh))
+    us_q = _time_op(lambda: pmg.nvfp4_quantize_rows(t["dgu"], *g))
+    us_dg = _time_op(lambda: pmg.nvfp4_grouped_gemm(*g, pdy["expert_offsets"], *q_gut, c=dxp))
+    bf = (op_ms["dgrad_down_gemm"] + op_ms["dgrad_gate_up_gemm"]) * 1e3
+    total = us_qp + us_dd + us_q + us_dg
+    out["nvfp4_input_gradient"] = {
+        "grad_quantize_permute": {"us": round(us_qp, 2)},
+        "dgrad_down_gemm": {"us": round(us_dd, 2), "TFLOPs": tf("dgrad_down_gemm", us_dd)},
+        "swiglu_grad_quantize": {"us": round(us_q, 2)},
+        "dgrad_gate_up_gemm": {"us": round(us_dg, 2), "TFLOPs": tf("dgrad_gate_up_gemm", us_dg)},
+        "total_us": round(total, 2), "bf16_dgrad_gemms_us": round(bf, 2),
+        "speedup_vs_bf16": round(bf / total, 3)}
+    out["how"] = ("after the timed steps: 3 untimed + 10 timed launches per op, HIP events on the "
+                  "launch stream; same routing, shapes and buffers as the step")
+    return out
 
 
 def practical_ceiling(gate_up_tflops, qp_gbps):

@@ -69,7 +69,7 @@ typedef enum nvfp4_status {
   NVFP4_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
   NVFP4_ERR_WORKSPACE = 4, /* workspace smaller than required */
   NVFP4_ERR_LAUNCH = 5,    /* the HIP runtime reported an error when enqueuing */
-  NVFP4_ERR_ARG = 6        /* an enumerated argument has an unknown value */
+  NVFP4_ERR_ARG = 6        /* an enumerated argument has an unknown value, or an output aliases an input */
 } nvfp4_status;
 
 #define NVFP4_DEVERR_BAD_EXPERT 1   /* an expert id outside [0, E): that entry takes no row */
@@ -256,6 +256,21 @@ NVFP4MOE_API int swiglu_backward(const float* gu, const float* dh, int64_t R_cap
                                  const int32_t* expert_offsets, int32_t E,
                                  const float* topk_w, const int32_t* row_to_tk,
                                  uint16_t* dgu, void* stream);
+
+/*
+ * bf16_transpose - out[b][j][i] = in[b][i][j] for `batches` bf16 matrices.
+ * Weight preparation for a lower-precision backward: the blog "miniTE NVFP4"
+ * (yuxiaoba.github.io, section "Two complementary interventions") keeps the
+ * backward's precision independent of the forward's and notes that a
+ * lower-bit backward is not automatically faster.  Its NVFP4 input-gradient
+ * GEMM contracts a forward weight [E][out][in] over `out`, so it quantises
+ * the transposed weight [E][in][out] along `out` (nvfp4_quantize_rows_tiled).
+ *   in  bf16 bits [batches][rows][cols]; out bf16 bits [batches][cols][rows]
+ * Requires rows % 8 == 0, cols % 8 == 0, rows * cols <= INT32_MAX,
+ * 0 <= batches <= 65535; out must not overlap in (out == in: NVFP4_ERR_ARG).
+ */
+NVFP4MOE_API int bf16_transpose(const uint16_t* in, int64_t batches, int64_t rows, int64_t cols,
+                                uint16_t* out, void* stream);
 
 /* Measurement aid (no part of the MoE computation): the device's practical
  * FP16 MFMA rate.  256 workgroups of 8 wavefronts (two per SIMD on a 256-CU

@@ -64,6 +64,7 @@ SIGNATURES = {
     "bf16_grouped_gemm_gather": ([_P, _I64, _P, _I32, _P, _I32, _I64, _P, _I32, _I64, _I64, _P, _P],
                                  _c.c_int),
     "swiglu_backward": ([_P, _P, _I64, _I64, _P, _I32, _P, _P, _P, _P], _c.c_int),
+    "bf16_transpose": ([_P, _I64, _I64, _I64, _P, _P], _c.c_int),
     "nvfp4moe_mfma_ceiling": ([_I64, _P, _P], _c.c_int),
 }
 
@@ -271,6 +272,16 @@ def permute_gather_bf16(x, expert_offsets, row_to_tk, k: int, out=None):
     _req(out, "out", _BF16)
     _check("permute_gather_bf16", load_library().permute_gather_bf16(
         _ptr(x), T, H, k, _ptr(expert_offsets), E, _ptr(row_to_tk), _ptr(out), _stream()))
+    return out
+
+
+def bf16_transpose(x, out=None):
+    """out[b] = x[b].T for bf16 x [B, rows, cols] (weight preparation).  Returns [B, cols, rows]."""
+    _req(x, "x", _BF16, 3)
+    B, rows, cols = x.shape
+    out = _empty((B, cols, rows), torch.bfloat16, x) if out is None else out
+    _req(out, "out", _BF16)
+    _check("bf16_transpose", load_library().bf16_transpose(_ptr(x), B, rows, cols, _ptr(out), _stream()))
     return out
 
 

@@ -116,6 +116,40 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(
   }
 }
 
+// out[b][j][i] = in[b][i][j] for a batch of bf16 matrices: 64 x 64 tiles
+// through LDS, 16-byte loads and stores (rows and columns multiples of 8).
+// Weight preparation for the NVFP4 input-gradient GEMM, which contracts a
+// forward weight over its output dimension and so quantises its transpose.
+constexpr int kTr = 64;
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
+                                                             int rows, int cols,
+                                                             uint16_t* __restrict__ out) {
+  __shared__ uint16_t tile[kTr][kTr + 2];
+  const int64_t mat = (int64_t)rows * cols * blockIdx.z;
+  const int r0 = blockIdx.y * kTr, c0 = blockIdx.x * kTr;
+  for (int q = threadIdx.x; q < kTr * 8; q += 256) {
+    const int r = q >> 3, ch = q & 7;
+    if (r0 + r < rows && c0 + 8 * ch < cols) {
+      const uint4 v = *reinterpret_cast<const uint4*>(in + mat + (int64_t)(r0 + r) * cols + c0 + 8 * ch);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tile[r][8 * ch + j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+    }
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < kTr * 8; q += 256) {
+    const int c = q >> 3, ch = q & 7;
+    if (c0 + c < cols && r0 + 8 * ch < rows) {
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = (uint32_t)tile[8 * ch + 2 * j][c] | ((uint32_t)tile[8 * ch + 2 * j + 1][c] << 16);
+      *reinterpret_cast<uint4*>(out + mat + (int64_t)(c0 + c) * rows + r0 + 8 * ch) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
 }  // namespace nvfp4moe
 
 using namespace nvfp4moe;
@@ -164,6 +198,21 @@ NVFP4MOE_API int swiglu_backward(const float* gu, const float* dh, int64_t R_cap
   hipStream_t s = static_cast<hipStream_t>(stream);
   swiglu_backward_kernel<<<(unsigned)((R_cap + kRows - 1) / kRows), 256, 0, s>>>(
       gu, dh, (int)I, expert_offsets, E, topk_w, row_to_tk, dgu);
+  return launch_status();
+}
+
+NVFP4MOE_API int bf16_transpose(const uint16_t* in, int64_t batches, int64_t rows, int64_t cols,
+                                uint16_t* out, void* stream) {
+  if (batches < 0 || batches > 65535 || rows < 0 || cols < 0 || rows % 8 != 0 || cols % 8 != 0)
+    return NVFP4_ERR_SHAPE;
+  if (rows > (int64_t)kTr * 65535 || cols > (int64_t)kTr * 65535 || rows * cols > INT32_MAX)
+    return NVFP4_ERR_SHAPE;
+  if (batches == 0 || rows == 0 || cols == 0) return NVFP4_OK;
+  if (!in || !out) return NVFP4_ERR_NULL;
+  if (!aligned16(in) || !aligned16(out)) return NVFP4_ERR_ALIGN;
+  if (in == out) return NVFP4_ERR_ARG;
+  const dim3 grid((unsigned)((cols + kTr - 1) / kTr), (unsigned)((rows + kTr - 1) / kTr), (unsigned)batches);
+  transpose_bf16_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(in, (int)rows, (int)cols, out);
   return launch_status();
 }
 

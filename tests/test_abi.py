@@ -25,7 +25,7 @@ def test_header_declares_the_entry_points():
     names = set(declared_functions())
     for n in ("nvfp4_quantize_permute", "nvfp4_grouped_gemm", "swiglu_quantize", "unpermute_combine",
               "nvfp4_quantize_rows", "bf16_grouped_gemm", "bf16_grouped_gemm_gather", "permute_gather_bf16",
-              "swiglu_backward"):
+              "swiglu_backward", "bf16_transpose"):
         assert n in names
 
 
@@ -125,6 +125,16 @@ def test_streaming_ops_host_checks(lib):
     assert lib.unpermute_combine(FAKE, 10, 8, 2048, None, None, FAKE, None) == ERR_NULL
     assert lib.permute_gather_bf16(FAKE, 10, 2048, 8, FAKE, 0, FAKE, FAKE, None) == ERR_SHAPE
     assert lib.swiglu_backward(FAKE, FAKE, 10, 768, FAKE, 4, None, None, FAKE + 2, None) == ERR_ALIGN
+
+
+def test_transpose_host_checks(lib):
+    assert lib.bf16_transpose(FAKE, 2, 12, 16, FAKE + 64, None) == ERR_SHAPE        # rows % 8
+    assert lib.bf16_transpose(FAKE, 65536, 8, 8, FAKE + 64, None) == ERR_SHAPE      # too many matrices
+    assert lib.bf16_transpose(FAKE, 1, 65536, 65536, FAKE + 64, None) == ERR_SHAPE  # rows * cols > INT32_MAX
+    assert lib.bf16_transpose(None, 0, 8, 8, None, None) == OK                      # nothing to do
+    assert lib.bf16_transpose(None, 1, 8, 8, FAKE, None) == ERR_NULL
+    assert lib.bf16_transpose(FAKE + 2, 1, 8, 8, FAKE + 64, None) == ERR_ALIGN
+    assert lib.bf16_transpose(FAKE, 1, 8, 8, FAKE, None) == ERR_ARG                 # in place
 
 
 def test_mfma_ceiling_host_checks(lib):
