@@ -30,7 +30,7 @@
 //     beyond one on the load width.
 //   * The activation tile is shared by the 8 wavefronts, so it is decoded once
 //     per K-step, cooperatively, into an FP16 tile in LDS (128 B rows, 16-byte
-//     chunks XOR-swizzled by row); each wavefront decodes only its own weight
+//     chunks XOR-swizzled by row pair); each wavefront decodes only its own weight
 //     fragments, in registers.  Both decodes of K-step g+1 are interleaved with
 //     the MFMAs of K-step g, so one barrier per K-step suffices.
 //   * Decoding is v_cvt_scalef32_pk_f16_fp4 plus one packed FP16 multiply by
@@ -83,7 +83,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 struct __align__(16) Stage {
   uint8_t a[BM * kRowB];       // 4 KiB FP4 activation codes, row-major
-  uint8_t w[BN * kRowB];       // 16 KiB FP4 weight codes, row-major (directly after a)
+  uint8_t w[BN * kRowB];       // 16 KiB FP4 weight codes (directly after a): per 32 rows, the
+                               // first 16 bytes of each row, then the last 16 (16 B per row)
   uint8_t as[BM * kScB];       // 512 B
   uint8_t ws[BN * kScB];       // 2 KiB (directly after as)
 };
@@ -96,8 +97,14 @@ struct __align__(16) Smem {
   int tile_start[NVFP4MOE_MAX_EXPERTS + 1];   // m-tiles before expert e
 };
 
-// byte offset of 16-byte chunk c (0..7) of row r in the FP16 activation tile
-__device__ __forceinline__ int a16_off(int r, int c) { return r * kA16Row + ((c ^ (r & 7)) << 4); }
+// byte offset of 16-byte chunk c (0..7) of row r in the FP16 activation tile.
+// An LDS pass serves 16 lanes of a 16-byte read; the fragment reads put rows
+// r..r+15 (r a multiple of 16) in one pass.  The 64 four-byte banks span 256
+// bytes, two 128-byte rows: even rows sit on one half of the banks, odd rows
+// on the other, so the chunk index is XORed with (r / 2) mod 8 and the 16 rows
+// fall on 16 distinct 16-byte bank groups (as do the decoder's writes: 4 rows
+// x 4 chunks per pass).
+__device__ __forceinline__ int a16_off(int r, int c) { return r * kA16Row + ((c ^ ((r >> 1) & 7)) << 4); }
 
 // E4M3 byte b (non-negative) -> two FP16 copies of b * 2^-8.  The 7 value bits
 // of E4M3 shifted up by 7 land exactly on FP16's exponent/mantissa fields with
@@ -249,7 +256,9 @@ void grouped_gemm_kernel(
   // Load cursor: the next K-step to load is (ltile, lk).  Each lane's sources
   // are 32-bit byte offsets from the operand bases (the host keeps every
   // operand under 4 GiB).  A wavefront instruction fills 1 KiB of LDS: 32 code
-  // rows (lane l -> row l/2, 16-byte half l%2) or 64 scale dwords.
+  // rows or 64 scale dwords.  Activation rows: lane l -> row l/2, 16-byte half
+  // l%2 (row-major).  Weight rows: lane l -> row l%32, half l/32, so that a
+  // fragment read (16 lanes: 16 rows, one half) covers 256 contiguous bytes.
   int lL = begin, lk = 0;
   uint32_t off_c[kCIW], off_s[kSIW];
   // Weight K-step strides: row-major [E][N][K/2] moves 32 code bytes (4 scale
@@ -283,8 +292,8 @@ void grouped_gemm_kernel(
       const uint32_t half16 = (lane & 1) * 16;
       const uint32_t wbase = (uint32_t)t.e * nk * N;
       auto wrow = [&](int q) __attribute__((always_inline)) {
-        const uint32_t n = (uint32_t)min(t.n0 + 32 * (q - BM / 32) + (lane >> 1), N - 1);
-        return (wbase + n) * kRowB + half16;
+        const uint32_t n = (uint32_t)min(t.n0 + 32 * (q - BM / 32) + (lane & 31), N - 1);
+        return (wbase + n) * kRowB + (lane >> 5) * 16;
       };
       vo0 = wave < 4 ? (uint32_t)min(t.m0 + 32 * wave + (lane >> 1), m_last) * kb + half16 : wrow(wave);
       vo1 = wrow(wave + 8);
@@ -301,9 +310,10 @@ void grouped_gemm_kernel(
       if (q < BM / 32) {
         off_c[u] = (uint32_t)min(t.m0 + 32 * q + (lane >> 1), m_last) * kb + half * 16;
       } else {
-        const uint32_t n = (uint32_t)min(t.n0 + 32 * (q - BM / 32) + (lane >> 1), N - 1);
-        off_c[u] = w_tiled ? ((uint32_t)t.e * nk * N + n) * kRowB + half * 16
-                           : ((uint32_t)t.e * N + n) * kb + half * 16;
+        const uint32_t n = (uint32_t)min(t.n0 + 32 * (q - BM / 32) + (lane & 31), N - 1);
+        const uint32_t wh = (lane >> 5) * 16;
+        off_c[u] = w_tiled ? ((uint32_t)t.e * nk * N + n) * kRowB + wh
+                           : ((uint32_t)t.e * N + n) * kb + wh;
       }
     }
 #pragma unroll
@@ -381,7 +391,7 @@ void grouped_gemm_kernel(
 #pragma unroll
     for (int f = 0; f < FB; ++f) {
       const int row = WN * wave + 32 * f + l32;
-      rb[f] = *reinterpret_cast<const uint4*>(S.w + row * kRowB + h * 16);
+      rb[f] = *reinterpret_cast<const uint4*>(S.w + (2 * wave + f) * 1024 + h * 512 + l32 * 16);
       xb[f] = *reinterpret_cast<const uint16_t*>(S.ws + row * kScB + h * 2);
     }
   };
