@@ -54,6 +54,8 @@ def _routed_case(T, H, E, k, N, kind, seed):
     (300, 512, 16, 2, 144, "zipf"),        # N not a multiple of the 128-column tile
     (64, 128, 32, 8, 16, "uniform"),       # smallest K step and N; many tiny experts
     (33, 384, 128, 8, 64, "zipf"),         # empty experts, 1-row experts
+    (100, 64, 8, 4, 96, "uniform"),        # K = 64: one K-step per tile
+    (2000, 64, 64, 8, 512, "zipf"),        # one K-step per tile, several tiles per workgroup
 ])
 def test_grouped_gemm_small_all_elements(T, H, E, k, N, kind):
     print(f"[gemm] T={T} H={H} E={E} k={k} N={N} {kind}", flush=True)
