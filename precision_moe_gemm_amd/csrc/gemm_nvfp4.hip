@@ -14,7 +14,7 @@
 // block-scaled FP4 MFMA takes one power-of-two scale per 32 elements and
 // cannot carry an E4M3 scale per 16 elements exactly.)
 //
-// Structure.  One 512-thread workgroup per CU (about 140 KiB of LDS), two
+// Structure.  One 512-thread workgroup per CU (about 157 KiB of LDS), two
 // wavefronts per SIMD.  Workgroup tile 128 x 512 (rows of one expert x output
 // columns), K-step 64; wavefront w owns the columns [64w, 64w+64) for all 128
 // rows as 4 x 2 MFMA 32x32x16 tiles.  The MFMA computes C^T tiles (weights as
@@ -89,12 +89,15 @@ struct __align__(16) Stage {
   uint8_t ws[BN * kScB];       // 2 KiB (directly after as)
 };
 
+constexpr int kMtCap = 8192;   // m-tiles whose expert the prologue tabulates in LDS
+
 struct __align__(16) Smem {
   Stage st[kStages];
   uint8_t a16[2][BM * kA16Row];   // 2 x 16 KiB decoded activations (FP16)
   uint8_t stg[kWaves][4096];      // per-wavefront staging of one 32 x 32 FP32 output tile
   float rs[2][BM + BN];            // row scales of a tile's rows, then of its weight rows (epilogue)
   int tile_start[NVFP4MOE_MAX_EXPERTS + 1];   // m-tiles before expert e
+  int16_t mt_expert[kMtCap];                  // expert of m-tile tm (when they fit)
 };
 
 // byte offset of 16-byte chunk c (0..7) of row r in the FP16 activation tile.
@@ -177,14 +180,22 @@ struct Tile {
   int e, m0, rows, n0;
 };
 
-__device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_start, int E,
-                                        const int32_t* __restrict__ offsets) {
-  const int tm = L / n_tiles, tn = L - tm * n_tiles;
+// the expert of m-tile tm: the last e with tile_start[e] <= tm
+__device__ __forceinline__ int expert_of(int tm, const int* tile_start, int E) {
   int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (tile_start[mid] <= tm) lo = mid; else hi = mid;
   }
+  return lo;
+}
+
+// mt_expert: the prologue's table of expert_of, or null when it did not fit
+__device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_start,
+                                        const int16_t* mt_expert, int E,
+                                        const int32_t* __restrict__ offsets) {
+  const int tm = L / n_tiles, tn = L - tm * n_tiles;
+  const int lo = mt_expert ? (int)mt_expert[tm] : expert_of(tm, tile_start, E);
   // the values are the same in every lane: keep them in scalar registers
   Tile t;
   t.e = __builtin_amdgcn_readfirstlane(lo);
@@ -228,7 +239,14 @@ void grouped_gemm_kernel(
   __syncthreads();
 
   const int n_tiles = (N + BN - 1) / BN;
-  const int total = __builtin_amdgcn_readfirstlane(sm.tile_start[E]) * n_tiles;
+  const int total_m = __builtin_amdgcn_readfirstlane(sm.tile_start[E]);
+  const int total = total_m * n_tiles;
+  // each tile's expert by one LDS read instead of a binary search
+  const int16_t* mt_tab = total_m <= kMtCap ? sm.mt_expert : nullptr;
+  if (mt_tab) {
+    for (int tm = tid; tm < total_m; tm += kThreads) sm.mt_expert[tm] = (int16_t)expert_of(tm, sm.tile_start, E);
+    __syncthreads();
+  }
   // XCD-contiguous tile ranges when the grid is a multiple of 8 workgroups
   // (workgroups go to the XCDs round-robin); the range's workgroups take its
   // tiles in turn
@@ -286,7 +304,7 @@ void grouped_gemm_kernel(
                                    : (uint32_t)offsetof(Stage, as) + (uint32_t)(wave - 6) * 256u;
   uint32_t vo0 = 0, vo1 = 0, vo2 = 0;
   auto set_load_tile = [&](int L) __attribute__((always_inline)) {
-    const Tile t = tile_at(L, n_tiles, sm.tile_start, E, offsets);
+    const Tile t = tile_at(L, n_tiles, sm.tile_start, mt_tab, E, offsets);
     if constexpr (KT) {
       const int m_last = t.m0 + t.rows - 1;
       const uint32_t half16 = (lane & 1) * 16;
@@ -564,7 +582,7 @@ void grouped_gemm_kernel(
 
   Tile prev{0, 0, 0, 0};
   for (int L = begin; L < end; L += step) {
-    const Tile t = tile_at(L, n_tiles, sm.tile_start, E, offsets);
+    const Tile t = tile_at(L, n_tiles, sm.tile_start, mt_tab, E, offsets);
     const int fa_eff = (t.rows + 31) >> 5;
     wait_vmcnt(n_last);
     lds_barrier();
