@@ -14,6 +14,7 @@ routing ids, offsets and identity maps ``torch.int32``.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import torch
@@ -104,7 +105,9 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-def _req(t, name, dtypes, ndim=None):
+def _req(t, name, dtypes, ndim=None, numel=None):
+    """Check a tensor argument; `numel`: the elements the library reads or writes
+    through it (the C-ABI sees only the pointer, so a smaller buffer is refused here)."""
     if t is None:
         return
     if not isinstance(t, torch.Tensor):
@@ -117,6 +120,8 @@ def _req(t, name, dtypes, ndim=None):
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs {numel}")
 
 
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
@@ -137,7 +142,8 @@ def nvfp4_quantize_rows(x, codes=None, bscales=None, rscales=None):
     codes = _empty((rows, K // 2), torch.uint8, x) if codes is None else codes
     bscales = _empty((rows, K // 16), torch.uint8, x) if bscales is None else bscales
     rscales = _empty((rows,), torch.float32, x) if rscales is None else rscales
-    _req(codes, "codes", _U8); _req(bscales, "bscales", _U8); _req(rscales, "rscales", _F32)
+    _req(codes, "codes", _U8, numel=rows * (K // 2)); _req(bscales, "bscales", _U8, numel=rows * (K // 16))
+    _req(rscales, "rscales", _F32, numel=rows)
     _check("nvfp4_quantize_rows", load_library().nvfp4_quantize_rows(
         _ptr(x), rows, K, _ptr(codes), _ptr(bscales), _ptr(rscales), _stream()))
     return codes, bscales, rscales
@@ -154,7 +160,8 @@ def nvfp4_quantize_rows_tiled(x, group_rows: int, codes=None, bscales=None, rsca
     codes = _empty((rows // G, K // 64, G, 32), torch.uint8, x) if codes is None else codes
     bscales = _empty((rows // G, K // 64, G, 4), torch.uint8, x) if bscales is None else bscales
     rscales = _empty((rows,), torch.float32, x) if rscales is None else rscales
-    _req(codes, "codes", _U8); _req(bscales, "bscales", _U8); _req(rscales, "rscales", _F32)
+    _req(codes, "codes", _U8, numel=rows * (K // 2)); _req(bscales, "bscales", _U8, numel=rows * (K // 16))
+    _req(rscales, "rscales", _F32, numel=rows)
     _check("nvfp4_quantize_rows_tiled", load_library().nvfp4_quantize_rows_tiled(
         _ptr(x), rows, K, G, _ptr(codes), _ptr(bscales), _ptr(rscales), _stream()))
     return codes, bscales, rscales
@@ -184,13 +191,11 @@ def nvfp4_quantize_permute(x, topk_ids, E: int, workspace=None, dev_err=None, ou
         raise ValueError("invalid routing shape")
     if workspace is None:
         workspace = _empty((max(ws_bytes, 256),), torch.uint8, x)
-    for name in ("codes", "bscales"):
-        _req(res[name], name, _U8)
-    _req(res["rscales"], "rscales", _F32)
-    for name in ("expert_offsets", "row_to_tk", "tk_to_row"):
-        _req(res[name], name, _I32T)
+    for name, (shp, _) in shapes.items():
+        _req(res[name], name, _U8 if name in ("codes", "bscales") else _F32 if name == "rscales" else _I32T,
+             numel=math.prod(shp))
     _req(workspace, "workspace", _U8)
-    _req(dev_err, "dev_err", _I32T)
+    _req(dev_err, "dev_err", _I32T, numel=1)
     _check("nvfp4_quantize_permute", load_library().nvfp4_quantize_permute(
         _ptr(x), T, H, _ptr(topk_ids), k, E, _ptr(res["codes"]), _ptr(res["bscales"]),
         _ptr(res["rscales"]), _ptr(res["expert_offsets"]), _ptr(res["row_to_tk"]),
@@ -219,8 +224,11 @@ def nvfp4_grouped_gemm(a_codes, a_bscales, a_rscales, expert_offsets, w_codes, w
         ok = w_codes.dim() == 3 and w_codes.shape[0] == E and w_codes.shape[2] * 2 == K
     if not ok:
         raise ValueError("w_codes/w_bscales shapes do not match E, K and a known layout")
+    _req(a_bscales, "a_bscales", _U8, numel=R_cap * (K // 16))
+    _req(a_rscales, "a_rscales", _F32, numel=R_cap)
+    _req(w_rscales, "w_rscales", _F32, numel=E * N)
     c = _empty((R_cap, N), torch.float32, a_codes) if c is None else c
-    _req(c, "c", _F32)
+    _req(c, "c", _F32, numel=R_cap * N)
     _check("nvfp4_grouped_gemm", load_library().nvfp4_grouped_gemm(
         _ptr(a_codes), _ptr(a_bscales), _ptr(a_rscales), _ptr(expert_offsets), E, R_cap,
         _ptr(w_codes), _ptr(w_bscales), _ptr(w_rscales), N, K, layout, _ptr(c), _stream()))
@@ -241,7 +249,9 @@ def swiglu_quantize(gu, expert_offsets, topk_w=None, row_to_tk=None, h_out=False
     bsc = o["bscales"] if "bscales" in o else _empty((R_cap, I // 16), torch.uint8, gu)
     rsc = o["rscales"] if "rscales" in o else _empty((R_cap,), torch.float32, gu)
     h = (o["h"] if "h" in o else _empty((R_cap, I), torch.float32, gu)) if h_out else None
-    _req(codes, "codes", _U8); _req(bsc, "bscales", _U8); _req(rsc, "rscales", _F32); _req(h, "h", _F32)
+    _req(codes, "codes", _U8, numel=R_cap * (I // 2)); _req(bsc, "bscales", _U8, numel=R_cap * (I // 16))
+    _req(rsc, "rscales", _F32, numel=R_cap); _req(h, "h", _F32, numel=R_cap * I)
+    _req(row_to_tk, "row_to_tk", _I32T, numel=R_cap)
     _check("swiglu_quantize", load_library().swiglu_quantize(
         _ptr(gu), R_cap, I, _ptr(expert_offsets), E, _ptr(topk_w), _ptr(row_to_tk),
         _ptr(codes), _ptr(bsc), _ptr(rsc), _ptr(h), _stream()))
@@ -255,8 +265,9 @@ def unpermute_combine(d, tk_to_row, k: int, topk_w=None, y=None):
     _req(topk_w, "topk_w", _F32)
     T = tk_to_row.numel() // k
     H = d.shape[1]
+    _req(topk_w, "topk_w", _F32, numel=T * k)
     y = _empty((T, H), torch.bfloat16, d) if y is None else y
-    _req(y, "y", _BF16)
+    _req(y, "y", _BF16, numel=T * H)
     _check("unpermute_combine", load_library().unpermute_combine(
         _ptr(d), T, k, H, _ptr(tk_to_row), _ptr(topk_w), _ptr(y), _stream()))
     return y
@@ -268,8 +279,9 @@ def permute_gather_bf16(x, expert_offsets, row_to_tk, k: int, out=None):
     _req(row_to_tk, "row_to_tk", _I32T)
     T, H = x.shape
     E = expert_offsets.numel() - 1
+    _req(row_to_tk, "row_to_tk", _I32T, numel=T * k)
     out = _empty((T * k, H), torch.bfloat16, x) if out is None else out
-    _req(out, "out", _BF16)
+    _req(out, "out", _BF16, numel=T * k * H)
     _check("permute_gather_bf16", load_library().permute_gather_bf16(
         _ptr(x), T, H, k, _ptr(expert_offsets), E, _ptr(row_to_tk), _ptr(out), _stream()))
     return out
@@ -280,7 +292,7 @@ def bf16_transpose(x, out=None):
     _req(x, "x", _BF16, 3)
     B, rows, cols = x.shape
     out = _empty((B, cols, rows), torch.bfloat16, x) if out is None else out
-    _req(out, "out", _BF16)
+    _req(out, "out", _BF16, numel=B * rows * cols)
     _check("bf16_transpose", load_library().bf16_transpose(_ptr(x), B, rows, cols, _ptr(out), _stream()))
     return out
 
@@ -297,7 +309,7 @@ def bf16_grouped_gemm(a, expert_offsets, w, w_layout: int = W_KN, c=None):
     if kw != K or w.shape[0] != E:
         raise ValueError("weight shape does not match a / expert_offsets")
     c = _empty((R_cap, N), torch.float32, a) if c is None else c
-    _req(c, "c", _F32)
+    _req(c, "c", _F32, numel=R_cap * N)
     _check("bf16_grouped_gemm", load_library().bf16_grouped_gemm(
         _ptr(a), _ptr(expert_offsets), E, R_cap, _ptr(w), w_layout, N, K, _ptr(c), _stream()))
     return c
@@ -319,7 +331,7 @@ def bf16_grouped_gemm_gather(a, row_to_tk, k: int, expert_offsets, w, w_layout: 
     if kw != K or w.shape[0] != E:
         raise ValueError("weight shape does not match a / expert_offsets")
     c = _empty((R_cap, N), torch.float32, a) if c is None else c
-    _req(c, "c", _F32)
+    _req(c, "c", _F32, numel=R_cap * N)
     _check("bf16_grouped_gemm_gather", load_library().bf16_grouped_gemm_gather(
         _ptr(a), T, _ptr(row_to_tk), k, _ptr(expert_offsets), E, R_cap, _ptr(w), w_layout, N, K,
         _ptr(c), _stream()))
@@ -334,8 +346,10 @@ def swiglu_backward(gu, dh, expert_offsets, topk_w=None, row_to_tk=None, dgu=Non
     _req(row_to_tk, "row_to_tk", _I32T)
     R_cap, I2 = gu.shape
     E = expert_offsets.numel() - 1
+    _req(dh, "dh", _F32, numel=R_cap * (I2 // 2))
+    _req(row_to_tk, "row_to_tk", _I32T, numel=R_cap)
     dgu = _empty((R_cap, I2), torch.bfloat16, gu) if dgu is None else dgu
-    _req(dgu, "dgu", _BF16)
+    _req(dgu, "dgu", _BF16, numel=R_cap * I2)
     _check("swiglu_backward", load_library().swiglu_backward(
         _ptr(gu), _ptr(dh), R_cap, I2 // 2, _ptr(expert_offsets), E, _ptr(topk_w),
         _ptr(row_to_tk), _ptr(dgu), _stream()))
@@ -348,6 +362,6 @@ def mfma_ceiling(iters: int, sink=None):
     Returns (sink, flops issued).  Timing is the caller's."""
     if sink is None:
         sink = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
-    _req(sink, "sink", _F32)
+    _req(sink, "sink", _F32, numel=256 * 512)
     _check("nvfp4moe_mfma_ceiling", load_library().nvfp4moe_mfma_ceiling(iters, _ptr(sink), _stream()))
     return sink, 256 * 8 * iters * 8 * 32768

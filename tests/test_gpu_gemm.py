@@ -137,3 +137,20 @@ def test_repeated_calls_are_identical():
     R = int(host(res["expert_offsets"])[-1])
     for o in outs[1:]:
         assert np.array_equal(o[:R], outs[0][:R])
+
+
+def test_binding_refuses_short_buffers():
+    """The C-ABI sees pointers only: the binding refuses an output (or a known
+    input) smaller than what the library would write (read), before any launch."""
+    print("[binding] short buffers", flush=True)
+    x = W.activations(64, 256, config=3, tensor=1)
+    a = pmg.nvfp4_quantize_rows(bf16_dev(x))
+    w = quantize_weights_gpu(W.gaussian_bf16((1, 128, 256), 1.0, 3, 2))
+    off = dev(np.array([0, 64], np.int32))
+    with pytest.raises(ValueError, match="needs"):
+        pmg.nvfp4_grouped_gemm(*a, off, *w, c=torch.empty(64 * 127, dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError, match="needs"):
+        pmg.nvfp4_quantize_rows(bf16_dev(x), codes=torch.empty(10, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError, match="needs"):
+        pmg.bf16_transpose(bf16_dev(x.reshape(1, 64, 256)), out=torch.empty(8, dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
