@@ -198,6 +198,7 @@ def main():
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
+    graph = graph_steps(step, args.steps, args.warmup, T)
     op_ms = {name: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]))
              for i, (name, _) in enumerate(ops)}
 
@@ -254,6 +255,7 @@ def main():
                    "qkv_n": S.qkv_n, "routing": args.routing, "routed_rows": Rr,
                    "parallelism": "single GPU"},
         "layer_tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "graph": graph,
         "per_op": per_op,
         "roofline": roofline,
         "setup_s": round(setup_s, 1),
@@ -267,6 +269,35 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_bits, ids_np, wgu_bits, S, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def graph_steps(step, steps, warmup, T):
+    """The same step captured once in a HIP graph and replayed `steps` times
+    after `warmup` replays (after the eager timed steps, outside them): the
+    whole-step time without the host's launch gaps between the kernels."""
+    import torch
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    st.record(stream)
+    for _ in range(steps):
+        g.replay()
+    en.record(stream)
+    torch.cuda.synchronize()
+    ms = st.elapsed_time(en) / steps
+    return {"ms_per_step": round(ms, 4), "layer_tokens_per_s": round(T / (ms * 1e-3), 1),
+            "how": "one step captured in a HIP graph, replayed; same ops, buffers and stream"}
 
 
 def _time_op(fn, reps=10):
