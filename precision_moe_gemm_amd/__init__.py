@@ -221,7 +221,8 @@ def nvfp4_grouped_gemm(a_codes, a_bscales, a_rscales, expert_offsets, w_codes, w
         ok = tuple(w_codes.shape) == (E, K // 64, N, 32) and tuple(w_bscales.shape) == (E, K // 64, N, 4)
     else:
         layout, N = W_ROWMAJOR, w_codes.shape[1]
-        ok = w_codes.dim() == 3 and w_codes.shape[0] == E and w_codes.shape[2] * 2 == K
+        ok = (w_codes.dim() == 3 and w_codes.shape[0] == E and w_codes.shape[2] * 2 == K
+              and w_bscales.numel() >= E * N * (K // 16))
     if not ok:
         raise ValueError("w_codes/w_bscales shapes do not match E, K and a known layout")
     _req(a_bscales, "a_bscales", _U8, numel=R_cap * (K // 16))
@@ -244,6 +245,8 @@ def swiglu_quantize(gu, expert_offsets, topk_w=None, row_to_tk=None, h_out=False
     R_cap, I2 = gu.shape
     I = I2 // 2
     E = expert_offsets.numel() - 1
+    # the kernel reads topk_w[row_to_tk[r]], and row_to_tk holds entries below R_cap
+    _req(topk_w, "topk_w", _F32, numel=R_cap)
     o = out or {}
     codes = o["codes"] if "codes" in o else _empty((R_cap, I // 2), torch.uint8, gu)
     bsc = o["bscales"] if "bscales" in o else _empty((R_cap, I // 16), torch.uint8, gu)
@@ -263,8 +266,12 @@ def unpermute_combine(d, tk_to_row, k: int, topk_w=None, y=None):
     _req(d, "d", _F32, 2)
     _req(tk_to_row, "tk_to_row", _I32T)
     _req(topk_w, "topk_w", _F32)
+    if k < 1 or tk_to_row.numel() % k:
+        raise ValueError("tk_to_row must hold T * k entries")
     T = tk_to_row.numel() // k
     H = d.shape[1]
+    # tk_to_row names rows below T * k (the routed rows of nvfp4_quantize_permute)
+    _req(d, "d", _F32, numel=T * k * H)
     _req(topk_w, "topk_w", _F32, numel=T * k)
     y = _empty((T, H), torch.bfloat16, d) if y is None else y
     _req(y, "y", _BF16, numel=T * H)
@@ -347,6 +354,7 @@ def swiglu_backward(gu, dh, expert_offsets, topk_w=None, row_to_tk=None, dgu=Non
     R_cap, I2 = gu.shape
     E = expert_offsets.numel() - 1
     _req(dh, "dh", _F32, numel=R_cap * (I2 // 2))
+    _req(topk_w, "topk_w", _F32, numel=R_cap)
     _req(row_to_tk, "row_to_tk", _I32T, numel=R_cap)
     dgu = _empty((R_cap, I2), torch.bfloat16, gu) if dgu is None else dgu
     _req(dgu, "dgu", _BF16, numel=R_cap * I2)

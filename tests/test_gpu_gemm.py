@@ -153,4 +153,22 @@ def test_binding_refuses_short_buffers():
         pmg.nvfp4_quantize_rows(bf16_dev(x), codes=torch.empty(10, dtype=torch.uint8, device="cuda"))
     with pytest.raises(ValueError, match="needs"):
         pmg.bf16_transpose(bf16_dev(x.reshape(1, 64, 256)), out=torch.empty(8, dtype=torch.bfloat16, device="cuda"))
+    # row-major weight block scales shorter than E * N * K/16
+    with pytest.raises(ValueError, match="layout"):
+        pmg.nvfp4_grouped_gemm(*a, off, w[0], w[1][:, :64], w[2])
+    # combine: d with fewer than T * k rows; tk_to_row not a multiple of k
+    t2r = dev(np.arange(16, dtype=np.int32))
+    with pytest.raises(ValueError, match="needs"):
+        pmg.unpermute_combine(torch.empty(15, 64, dtype=torch.float32, device="cuda"), t2r, 4)
+    with pytest.raises(ValueError, match="T \\* k"):
+        pmg.unpermute_combine(torch.empty(16, 64, dtype=torch.float32, device="cuda"), t2r, 3)
+    # SwiGLU passes: router weights for fewer than R_cap entries
+    gu = torch.zeros(16, 64, dtype=torch.float32, device="cuda")
+    off16 = dev(np.array([0, 16], np.int32))
+    r2t = dev(np.arange(16, dtype=np.int32))
+    short_w = torch.ones(15, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="needs"):
+        pmg.swiglu_quantize(gu, off16, short_w, r2t)
+    with pytest.raises(ValueError, match="needs"):
+        pmg.swiglu_backward(gu, torch.zeros(16, 32, dtype=torch.float32, device="cuda"), off16, short_w, r2t)
     torch.cuda.synchronize()
