@@ -61,6 +61,7 @@ extern "C" {
 #define NVFP4MOE_MAX_K 8192      /* longest quantised row */
 #define NVFP4MOE_MAX_EXPERTS 1024
 #define NVFP4MOE_MAX_TOPK 32
+#define NVFP4MOE_NOALLOC_MAX_ENTRIES (1 << 20)   /* T * k limit of nvfp4_quantize_permute_noalloc */
 
 typedef enum nvfp4_status {
   NVFP4_OK = 0,
@@ -69,7 +70,8 @@ typedef enum nvfp4_status {
   NVFP4_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned */
   NVFP4_ERR_WORKSPACE = 4, /* workspace smaller than required */
   NVFP4_ERR_LAUNCH = 5,    /* the HIP runtime reported an error when enqueuing */
-  NVFP4_ERR_ARG = 6        /* an enumerated argument has an unknown value, or an output aliases an input */
+  NVFP4_ERR_ARG = 6,       /* an enumerated argument has an unknown value, or an output aliases an input */
+  NVFP4_ERR_SCRATCH = 7    /* the problem exceeds the fixed device scratch of an allocation-free entry point */
 } nvfp4_status;
 
 #define NVFP4_DEVERR_BAD_EXPERT 1   /* an expert id outside [0, E): that entry takes no row */
@@ -141,6 +143,29 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
                                         int32_t* tk_to_row, void* workspace,
                                         size_t workspace_bytes, int32_t* dev_err,
                                         void* stream);
+
+/*
+ * nvfp4_quantize_permute_noalloc - nvfp4_quantize_permute without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a device array inside the library sized for
+ * T * k <= NVFP4MOE_NOALLOC_MAX_ENTRIES routing entries and up to
+ * NVFP4MOE_MAX_EXPERTS experts (5.2 MB, held by every device the library runs
+ * on until the process ends); its device address is looked up on the first
+ * call on each device.  This entry point allocates nothing and calls no
+ * allocating routine.  Arguments, outputs, row order and errors are those of
+ * nvfp4_quantize_permute; T * k above NVFP4MOE_NOALLOC_MAX_ENTRIES returns
+ * NVFP4_ERR_SCRATCH and enqueues nothing.  Every call on one device shares
+ * that device's scratch (each call writes what it reads, so nothing carries
+ * over between calls): calls that overlap in time on one device (different
+ * streams, no ordering between them) race and give wrong results.
+ */
+NVFP4MOE_API int nvfp4_quantize_permute_noalloc(const uint16_t* x, int64_t T, int64_t H,
+                                                const int32_t* topk_ids, int32_t k, int32_t E,
+                                                uint8_t* codes, uint8_t* bscales, float* rscales,
+                                                int32_t* expert_offsets, int32_t* row_to_tk,
+                                                int32_t* tk_to_row, int32_t* dev_err,
+                                                void* stream);
 
 /*
  * nvfp4_grouped_gemm - grouped W4A4 expert GEMM on the expert-grouped buffer:

@@ -55,6 +55,8 @@ SIGNATURES = {
     "nvfp4_quantize_rows": ([_P, _I64, _I64, _P, _P, _P, _P], _c.c_int),
     "nvfp4_quantize_permute": ([_P, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                                 _c.c_size_t, _P, _P], _c.c_int),
+    "nvfp4_quantize_permute_noalloc": ([_P, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P],
+                                       _c.c_int),
     "nvfp4_quantize_rows_tiled": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], _c.c_int),
     "nvfp4_grouped_gemm": ([_P, _P, _P, _P, _I32, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _P],
                            _c.c_int),
@@ -201,6 +203,37 @@ def nvfp4_quantize_permute(x, topk_ids, E: int, workspace=None, dev_err=None, ou
         _ptr(res["rscales"]), _ptr(res["expert_offsets"]), _ptr(res["row_to_tk"]),
         _ptr(res["tk_to_row"]), _ptr(workspace), workspace.numel(), _ptr(dev_err), _stream()))
     return res
+
+
+NOALLOC_MAX_ENTRIES = 1 << 20
+_QP_OUTPUTS = ("codes", "bscales", "rscales", "expert_offsets", "row_to_tk", "tk_to_row")
+
+
+def nvfp4_quantize_permute_noalloc(x, topk_ids, E: int, out, dev_err=None):
+    """nvfp4_quantize_permute without a workspace and without any allocation: the
+    library's fixed device scratch serves T*k <= NOALLOC_MAX_ENTRIES entries.  Every
+    output must be given in `out` (same names and sizes as nvfp4_quantize_permute's
+    result); returns `out`.  Calls on one device that overlap in time race."""
+    _req(x, "x", _BF16, 2)
+    _req(topk_ids, "topk_ids", _I32T, 2)
+    T, H = x.shape
+    k = topk_ids.shape[1]
+    if topk_ids.shape[0] != T:
+        raise ValueError("topk_ids must have one row per token")
+    missing = [n for n in _QP_OUTPUTS if n not in out]
+    if missing:
+        raise ValueError(f"the allocation-free call needs every output given: missing {missing}")
+    R = T * k
+    need = {"codes": (R * (H // 2), _U8), "bscales": (R * (H // 16), _U8), "rscales": (R, _F32),
+            "expert_offsets": (E + 1, _I32T), "row_to_tk": (R, _I32T), "tk_to_row": (R, _I32T)}
+    for name, (n, dt) in need.items():
+        _req(out[name], name, dt, numel=n)
+    _req(dev_err, "dev_err", _I32T, numel=1)
+    _check("nvfp4_quantize_permute_noalloc", load_library().nvfp4_quantize_permute_noalloc(
+        _ptr(x), T, H, _ptr(topk_ids), k, E, _ptr(out["codes"]), _ptr(out["bscales"]),
+        _ptr(out["rscales"]), _ptr(out["expert_offsets"]), _ptr(out["row_to_tk"]),
+        _ptr(out["tk_to_row"]), _ptr(dev_err), _stream()))
+    return out
 
 
 def nvfp4_grouped_gemm(a_codes, a_bscales, a_rscales, expert_offsets, w_codes, w_bscales,

@@ -18,6 +18,7 @@
 #include "common.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace nvfp4moe {
 
@@ -761,6 +762,8 @@ NVFP4MOE_API const char* nvfp4moe_status_string(int status) {
     case NVFP4_ERR_WORKSPACE: return "workspace too small";
     case NVFP4_ERR_LAUNCH: return "the HIP runtime reported an error when enqueuing";
     case NVFP4_ERR_ARG: return "an enumerated argument has an unknown value";
+    case NVFP4_ERR_SCRATCH:
+      return "more routing entries (T * k) than the allocation-free entry point's fixed device scratch holds";
     default: return "unknown status";
   }
 }
@@ -811,12 +814,18 @@ NVFP4MOE_API int nvfp4_quantize_rows_tiled(const uint16_t* x, int64_t rows, int6
   return launch_status();
 }
 
-NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
-                                        const int32_t* topk_ids, int32_t k, int32_t E,
-                                        uint8_t* codes, uint8_t* bscales, float* rscales,
-                                        int32_t* expert_offsets, int32_t* row_to_tk,
-                                        int32_t* tk_to_row, void* workspace,
-                                        size_t workspace_bytes, int32_t* dev_err, void* stream) {
+}  // extern "C"
+
+namespace nvfp4moe {
+
+// The route + permute + quantise pass on a caller-given workspace (the count
+// table, then one rank per routing entry; every word is written before it is
+// read, so the workspace needs no clearing).
+static int quantize_permute_impl(const uint16_t* x, int64_t T, int64_t H, const int32_t* topk_ids,
+                                 int32_t k, int32_t E, uint8_t* codes, uint8_t* bscales,
+                                 float* rscales, int32_t* expert_offsets, int32_t* row_to_tk,
+                                 int32_t* tk_to_row, void* workspace, size_t workspace_bytes,
+                                 int32_t* dev_err, void* stream) {
   if (T < 0 || H <= 0 || H % 16 != 0 || H > NVFP4MOE_MAX_K) return NVFP4_ERR_SHAPE;
   if (E < 1 || E > NVFP4MOE_MAX_EXPERTS || k < 1 || k > E || k > NVFP4MOE_MAX_TOPK)
     return NVFP4_ERR_SHAPE;
@@ -883,6 +892,64 @@ NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
 #undef QR_LAUNCH
   }
   return launch_status();
+}
+
+// Scratch of the allocation-free entry point: the workspace of
+// quantize_permute_impl for up to NVFP4MOE_NOALLOC_MAX_ENTRIES routing entries
+// and NVFP4MOE_MAX_EXPERTS experts, as a device array of the library (each
+// device holds its own copy while the process lives).  Host code never passes
+// the array's name to a kernel: it stands for the host-side shadow, so the
+// device address is looked up once per device and kept in scratch_ptr.
+constexpr int64_t kNoAllocWords =
+    (int64_t)((NVFP4MOE_NOALLOC_MAX_ENTRIES + kPlanChunk - 1) >> kPlanChunkLog) * NVFP4MOE_MAX_EXPERTS +
+    NVFP4MOE_NOALLOC_MAX_ENTRIES;
+static __device__ __align__(256) int32_t scratch[kNoAllocWords];
+
+constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void* scratch_ptr[kMaxDevices];
+
+// device address of `scratch` on the current device (looked up on the first
+// call there); null if the runtime reports an error
+static void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace nvfp4moe
+
+extern "C" {
+
+NVFP4MOE_API int nvfp4_quantize_permute(const uint16_t* x, int64_t T, int64_t H,
+                                        const int32_t* topk_ids, int32_t k, int32_t E,
+                                        uint8_t* codes, uint8_t* bscales, float* rscales,
+                                        int32_t* expert_offsets, int32_t* row_to_tk,
+                                        int32_t* tk_to_row, void* workspace,
+                                        size_t workspace_bytes, int32_t* dev_err, void* stream) {
+  return quantize_permute_impl(x, T, H, topk_ids, k, E, codes, bscales, rscales, expert_offsets,
+                               row_to_tk, tk_to_row, workspace, workspace_bytes, dev_err, stream);
+}
+
+NVFP4MOE_API int nvfp4_quantize_permute_noalloc(const uint16_t* x, int64_t T, int64_t H,
+                                                const int32_t* topk_ids, int32_t k, int32_t E,
+                                                uint8_t* codes, uint8_t* bscales, float* rscales,
+                                                int32_t* expert_offsets, int32_t* row_to_tk,
+                                                int32_t* tk_to_row, int32_t* dev_err,
+                                                void* stream) {
+  if (T < 0 || k < 1) return NVFP4_ERR_SHAPE;
+  if (T * (int64_t)k > NVFP4MOE_NOALLOC_MAX_ENTRIES) return NVFP4_ERR_SCRATCH;
+  void* ws = scratch_on_current_device();
+  if (!ws) return NVFP4_ERR_LAUNCH;
+  return quantize_permute_impl(x, T, H, topk_ids, k, E, codes, bscales, rscales, expert_offsets,
+                               row_to_tk, tk_to_row, ws, (size_t)kNoAllocWords * sizeof(int32_t),
+                               dev_err, stream);
 }
 
 NVFP4MOE_API int swiglu_quantize(const float* gu, int64_t R_cap, int64_t I,

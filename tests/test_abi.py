@@ -13,7 +13,7 @@ import precision_moe_gemm_amd as pmg
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nvfp4moe.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH, ERR_ARG = range(7)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH, ERR_ARG, ERR_SCRATCH = range(8)
 
 
 def declared_functions():
@@ -37,8 +37,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.nvfp4moe_abi_version() == 1
-    for s in range(7):
-        assert pmg.status_string(s)
+    for s in range(8):
+        assert pmg.status_string(s) and pmg.status_string(s) != pmg.status_string(99)
     assert "unknown" in pmg.status_string(99)
 
 
@@ -78,6 +78,14 @@ def test_quantize_permute_host_checks(lib):
     assert f(*args(wsb=ws - 1)) == ERR_WORKSPACE
     assert f(*args(x=FAKE + 8)) == ERR_ALIGN
     assert f(*args(T=1 << 27, k=8, wsb=1 << 40)) == ERR_SHAPE   # T k above INT32_MAX / 2
+
+
+def test_quantize_permute_noalloc_host_checks(lib):
+    f = lib.nvfp4_quantize_permute_noalloc
+    big = (1 << 20) // 8 + 1                                # T * k one chunk past the scratch
+    assert f(FAKE, big, 256, FAKE, 8, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SCRATCH
+    assert f(FAKE, -1, 256, FAKE, 8, 128, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert "scratch" in pmg.status_string(ERR_SCRATCH)
 
 
 def test_gemm_host_checks(lib):
