@@ -32,22 +32,12 @@ __device__ __forceinline__ float e4m3_decode_nonneg(uint32_t b) {
   return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
 
-// E2M1 code of r: nearest grid value of |r| in {0,.5,1,1.5,2,3,4,6}, ties to
-// the even index, saturating at 6; bit 3 = sign bit of r.  Each comparison
-// adds one index; '>' at a midpoint whose lower neighbour has an even index,
-// '>=' where the upper neighbour is even.
-__device__ __forceinline__ uint32_t e2m1_encode(float r) {
-  float m = __builtin_fabsf(r);
-  uint32_t idx = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
-                 (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
-                 (uint32_t)(m > 5.0f);
-  return idx | ((__float_as_uint(r) >> 28) & 8u);
-}
-
 // Eight ratios -> eight E2M1 codes packed into one word (element j at bits
-// 4j..4j+3) with v_cvt_scalef32_pk_fp4_f32, scale 1.0.  The hardware
-// conversion was compared with e2m1_encode on every one of the 2^32 float32
-// bit patterns (NaNs excepted), for both signs, on gfx950: identical.
+// 4j..4j+3) with v_cvt_scalef32_pk_fp4_f32, scale 1.0: nearest grid value of
+// |r| in {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even grid index, saturating
+// at 6, sign bit of r in bit 3.  (The quantiser's GPU tests compare its codes
+// with the definition on every bf16 value up to 6 as an exact ratio, which
+// covers each tie and its neighbours, and on random rows.)
 __device__ __forceinline__ uint32_t e2m1_pack8(const float (&r)[8]) {
   uint32_t w = 0;
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[0], r[1], 1.0f, 0);
@@ -55,13 +45,6 @@ __device__ __forceinline__ uint32_t e2m1_pack8(const float (&r)[8]) {
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[4], r[5], 1.0f, 2);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, r[6], r[7], 1.0f, 3);
   return w;
-}
-
-// Code of element x in a block with dequantisation step d = b * s.  d == 0
-// (zero row or a block scale that underflowed) gives a zero of x's sign.
-__device__ __forceinline__ uint32_t e2m1_of(float x, float d) {
-  float r = d != 0.0f ? x / d : x * 0.0f;
-  return e2m1_encode(r);
 }
 
 // ------------------------------------------------------------------ wave ops

@@ -3,7 +3,7 @@ import numpy as np
 import torch
 
 import precision_moe_gemm_amd as pmg
-from oracle import quantize as oq
+from oracle import formats as of, quantize as oq
 
 DEV = "cuda:0"
 
@@ -84,3 +84,28 @@ def sample_rows(offsets: np.ndarray, experts, extra: int, seed: int):
     chosen = list(experts) + [int(e) for e in rng.choice(E, size=min(extra, E), replace=False)]
     rows = [np.arange(offsets[e], offsets[e + 1]) for e in chosen]
     return np.unique(np.concatenate(rows).astype(np.int64)), sorted(set(chosen))
+
+
+def bf16_midpoint_adjacent(x64, rel=2.0 ** -40):
+    """True where x lies within rel*|x| of a bf16 rounding midpoint (neighbours from the bit pattern)."""
+    b = of.round_to_bf16(x64).astype(np.int32)
+    mag = b & 0x7FFF
+    sign = b & 0x8000
+    q = of.bf16_to_f32(b.astype(np.uint16)).astype(np.float64)
+    up = of.bf16_to_f32((sign | np.minimum(mag + 1, 0x7F7F)).astype(np.uint16)).astype(np.float64)
+    dn = of.bf16_to_f32((sign | np.maximum(mag - 1, 0)).astype(np.uint16)).astype(np.float64)
+    dist = np.minimum(np.abs(x64 - (q + up) / 2), np.abs(x64 - (q + dn) / 2))
+    return dist <= rel * np.maximum(np.abs(x64), 1e-300)
+
+
+class BF16Experts:
+    """Per-expert float32 view of bf16 expert weights [E, ...] for the oracle's
+    bf16 GEMM, converted only for the experts it touches (the whole tensor
+    would not fit host memory in float)."""
+
+    def __init__(self, bits):
+        self.bits = bits
+        self.shape = bits.shape
+
+    def __getitem__(self, e):
+        return of.bf16_to_f32(self.bits[e])

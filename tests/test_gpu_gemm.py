@@ -78,9 +78,10 @@ def test_gate_up_full_size_sampled(kind):
 
 
 def test_down_shape_sampled():
-    """K=768, N=2048 over 128 experts (the down projection's shape)."""
+    """K=768, N=2048 over 128 experts (the down projection's shape), 4096 tokens:
+    about 256 rows per expert, so the sampled experts hold full 128-row tiles."""
     print("[gemm] down shape", flush=True)
-    T, E, k, I, H = 1024, 128, 8, 768, 2048
+    T, E, k, I, H = 4096, 128, 8, 768, 2048
     x = W.activations(T, I, config=W.CFG_DOWN)
     ids, _ = W.make_routing("softmax", T, E, k, W.CFG_DOWN)
     w_bits = W.gaussian_bf16((E, H, I), 0.02, W.CFG_DOWN, 21)
@@ -88,7 +89,9 @@ def test_down_shape_sampled():
     w = quantize_weights_gpu(w_bits)
     c = host(pmg.nvfp4_grouped_gemm(res["codes"], res["bscales"], res["rscales"], res["expert_offsets"], *w))
     (off, _, _), a_ref = ol.quantize_permute_ref(x, ids, E)
-    rows, experts = sample_rows(off, [0, 5, 127], extra=5, seed=2)
+    counts = np.diff(off)
+    assert counts.max() >= 256
+    rows, experts = sample_rows(off, [0, 5, 127, int(np.argmax(counts))], extra=5, seed=2)
     ref, bound = og.grouped_gemm_ref(*a_ref, off, *quantize_weights_oracle(w_bits, experts), rows=rows)
     print("  err/bound", assert_within(c[rows], ref, bound, "down"))
 
@@ -172,3 +175,35 @@ def test_binding_refuses_short_buffers():
     with pytest.raises(ValueError, match="needs"):
         pmg.swiglu_backward(gu, torch.zeros(16, 32, dtype=torch.float32, device="cuda"), off16, short_w, r2t)
     torch.cuda.synchronize()
+
+
+def test_more_m_tiles_than_the_lds_table():
+    """Over 8192 m-tiles of 128 rows: each tile's expert then comes from a binary
+    search over the experts' first m-tiles instead of the prologue's LDS table.
+    Rows are batch-invariant, so the result must equal, bit for bit, separate
+    launches per expert (each within the table's reach), and the oracle on
+    sampled rows.  Activations are random valid NVFP4 bytes made on the device."""
+    print("[gemm] > 8192 m-tiles (search path)", flush=True)
+    K, N = 64, 16
+    sizes = [400_000, 1, 649_215]                       # 3125 + 1 + 5072 = 8198 m-tiles
+    R = sum(sizes)
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    codes = torch.randint(0, 256, (R, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    bsc = torch.randint(0x28, 0x48, (R, K // 16), dtype=torch.uint8, device="cuda", generator=g)
+    rsc = torch.rand(R, device="cuda", generator=g) + 0.5
+    w_bits = W.gaussian_bf16((3, N, K), 0.02, 43, 1)
+    w = quantize_weights_gpu(w_bits)
+    full = pmg.nvfp4_grouped_gemm(codes, bsc, rsc, dev(off), *w)
+    for e in range(3):
+        lo, hi = int(off[e]), int(off[e + 1])
+        part = pmg.nvfp4_grouped_gemm(codes[lo:hi].clone(), bsc[lo:hi].clone(), rsc[lo:hi].clone(),
+                                      dev(np.array([0, hi - lo], np.int32)), *(t[e:e + 1].clone() for t in w))
+        assert torch.equal(part.view(torch.int32), full[lo:hi].view(torch.int32)), f"expert {e}"
+    rows = np.unique(np.concatenate([np.arange(0, 200), np.arange(399_990, 400_010),
+                                     np.arange(R - 300, R), np.random.default_rng(4).integers(0, R, 200)]))
+    a_h = (host(codes[rows]), host(bsc[rows]), host(rsc[rows]))
+    e_of = np.searchsorted(off, rows, side="right") - 1
+    sub_off = np.searchsorted(e_of, np.arange(4)).astype(np.int64)
+    ref, bound = og.grouped_gemm_ref(*a_h, sub_off, *quantize_weights_oracle(w_bits))
+    print("  err/bound", assert_within(host(full)[rows], ref, bound, "search path"))

@@ -77,6 +77,30 @@ def test_quantize_rows_edge_values():
     _check_rows(W.f32_to_bf16_bits(worked[None]), "worked example")
 
 
+def test_quantize_rows_e2m1_encode_sweep():
+    """Every bf16 value of magnitude up to 6, both signs, as an exact quotient
+    x / d: the row amax 2688 makes s = 1, and every other block holds a +-6, so
+    its scale is E4M3(1) and d = 1.  The codes then are the E2M1 encoding of
+    each bf16 value itself (every tie, and every bf16 neighbour of a tie)."""
+    bits = np.arange(0, 0x8000, dtype=np.uint32)
+    vals = W.bf16_bits_to_f32(bits.astype(np.uint16))
+    mags = vals[np.isfinite(vals) & (vals <= 6.0)]
+    sweep = np.concatenate([mags, -mags]).astype(np.float32)
+    per_row = 127 * 15                                   # 127 blocks of 15 sweep values after the 2688 block
+    n_rows = -(-sweep.size // per_row)
+    sweep = np.concatenate([sweep, np.zeros(n_rows * per_row - sweep.size, np.float32)])
+    rows = np.zeros((n_rows, 2048), np.float32)
+    rows[:, 0] = 2688.0
+    blocks = rows[:, 16:].reshape(n_rows, 127, 16)
+    blocks[:, :, 0] = np.where(np.arange(127) % 2 == 0, 6.0, -6.0)
+    blocks[:, :, 1:] = sweep.reshape(n_rows, 127, 15)
+    x = W.f32_to_bf16_bits(rows)
+    assert np.array_equal(W.bf16_bits_to_f32(x), rows)  # every value is a bf16 value
+    _check_rows(x, "E2M1 encode sweep")
+    c, b, s = oq.quantize_rows_bf16(x)
+    assert np.all(s == 1.0) and np.all(b[:, 1:] == 0x38)  # d = 1 in every sweep block
+
+
 def _check_permute(x_bits, ids, E, tag, dev_err_expected=0):
     print(f"[quantize_permute] {tag} T={x_bits.shape[0]} H={x_bits.shape[1]} k={ids.shape[1]} E={E}", flush=True)
     err = torch.zeros(1, dtype=torch.int32, device="cuda:0")

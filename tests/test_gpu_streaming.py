@@ -6,8 +6,10 @@ the sigmoid from a refined reciprocal and multiplies where the oracle divides,
 so its float64 values may differ from the oracle's by a few ulps.  That can
 change a float32 (bf16) rounding only when the oracle's float64 value lies
 within a few float64 ulps of a rounding midpoint.  Those elements (found by
-the oracle alone) are listed; every other element must match bit for bit, and
-every row without such an element must give bit-identical NVFP4 bytes.
+the oracle alone) are listed; every other element must match bit for bit.
+The NVFP4 bytes of every row must equal the oracle's quantiser applied to the
+GPU's own h (so rows holding such an element are checked too), and those of
+rows without one must also equal the oracle's from its own h.
 Combine and gather: bit-exact.  BF16 GEMM: 2e-5 * sum |a w|.
 """
 import numpy as np
@@ -16,23 +18,12 @@ import torch
 
 import precision_moe_gemm_amd as pmg
 import workloads as W
-from oracle import combine as oc, formats as of, gemm as og, permute as op, swiglu as osw
-from helpers import assert_within, bf16_dev, bf16_host, dev, host, gpu_ready, sample_rows
+from oracle import combine as oc, formats as of, gemm as og, permute as op, quantize as oq, swiglu as osw
+from helpers import (assert_within, bf16_dev, bf16_host, bf16_midpoint_adjacent as _bf16_midpoint_adjacent,
+                     dev, host, gpu_ready, sample_rows)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_ready(), reason="needs a GPU")]
-
-
-def _bf16_midpoint_adjacent(x64, rel=2.0 ** -40):
-    """True where x lies within rel*|x| of a bf16 rounding midpoint (neighbours from the bit pattern)."""
-    b = of.round_to_bf16(x64).astype(np.int32)
-    mag = b & 0x7FFF
-    sign = b & 0x8000
-    q = of.bf16_to_f32(b.astype(np.uint16)).astype(np.float64)
-    up = of.bf16_to_f32((sign | np.minimum(mag + 1, 0x7F7F)).astype(np.uint16)).astype(np.float64)
-    dn = of.bf16_to_f32((sign | np.maximum(mag - 1, 0)).astype(np.uint16)).astype(np.float64)
-    dist = np.minimum(np.abs(x64 - (q + up) / 2), np.abs(x64 - (q + dn) / 2))
-    return dist <= rel * np.maximum(np.abs(x64), 1e-300)
 
 
 def _routing(T, E, k, kind, seed):
@@ -60,8 +51,14 @@ def test_swiglu_quantize(T, E, k, I, weighted):
     gh = host(h)
     same = gh.view(np.uint32) == rh.view(np.uint32)
     assert np.all(same | amb), f"h differs off the midpoints at {np.argwhere(~(same | amb))[:5].tolist()}"
+    # every row: the GPU's bytes are the oracle's quantiser of the GPU's own h
+    oc_, ob_, os_ = oq.quantize_rows_f32(gh)
+    R_ = int(off[-1])
+    assert np.array_equal(host(codes)[:R_], oc_[:R_])
+    assert np.array_equal(host(bsc)[:R_], ob_[:R_])
+    assert np.array_equal(host(rsc)[:R_].view(np.uint32), os_[:R_].view(np.uint32))
     clean = ~amb.any(axis=1)
-    print(f"  midpoint-adjacent elements: {int(amb.sum())}, rows excluded: {int((~clean).sum())}")
+    print(f"  midpoint-adjacent elements: {int(amb.sum())} in {int((~clean).sum())} rows")
     assert np.array_equal(host(codes)[clean], rc[clean])
     assert np.array_equal(host(bsc)[clean], rb[clean])
     assert np.array_equal(host(rsc)[clean].view(np.uint32), rs[clean].view(np.uint32))
