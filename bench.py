@@ -198,7 +198,16 @@ def main():
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(stop)
     ms_step = ms_total / args.steps
+    # the same steps with no per-op events, as the baseline of the graph replay
+    torch.cuda.synchronize()
+    start.record(stream)
+    for s in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step_plain = start.elapsed_time(stop) / args.steps
     graph = graph_steps(step, args.steps, args.warmup, T)
+    graph["eager_ms_per_step_no_events"] = round(ms_step_plain, 4)
     op_ms = {name: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]))
              for i, (name, _) in enumerate(ops)}
 
@@ -220,6 +229,13 @@ def main():
         "swiglu_backward": Rr * 2 * I * 4 + Rr * I * 4 + Rr * 8 + Rr * 2 * I * 2,
         "dgrad_combine": Rr * H * 4 + T * k * 4 + T * H * 2,
     }
+    # quantize-permute with x out of the caches: a 512 MiB write between launches
+    # (outside the timed events) evicts the 256 MB last-level cache, so x and
+    # the routing come from HBM, as they would after the attention block
+    qp_cold_us = time_cold(ops[2][1], reps=args.steps)
+    op_ms_in_step = dict(op_ms)
+    op_ms["quantize_permute"] = qp_cold_us * 1e-3
+
     per_op = {}
     for name in op_ms:
         us = op_ms[name] * 1e3
@@ -231,6 +247,9 @@ def main():
             gbs = op_bytes[name] / (us * 1e-6) / 1e9
             d.update(GBps=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBPS, 4))
         per_op[name] = d
+    per_op["quantize_permute"]["in_step_us"] = round(op_ms_in_step["quantize_permute"] * 1e3, 2)
+    per_op["quantize_permute"]["how"] = ("mean over --steps launches, each after a 512 MiB cache-evicting "
+                                         "write outside its events; in_step_us: inside the timed step")
 
     w4_us = (op_ms["gate_up_gemm"] + op_ms["down_gemm"]) * 1e3
     value = (gemm_flops["gate_up_gemm"] + gemm_flops["down_gemm"]) / (w4_us * 1e-6) / 1e12
@@ -261,6 +280,8 @@ def main():
         "setup_s": round(setup_s, 1),
     }
 
+    result["gate_up_by_routing"] = gate_up_by_routing(
+        args.routing, gu_us, dict(x=x, E=E, k=k, I=I, H=H, T=T, q_gu=q_gu, gu=gu, ws=ws, cfg=cfg), args.steps)
     result["practical_ceiling"] = practical_ceiling(gu_tf, per_op["quantize_permute"]["GBps"])
     if not args.no_comparisons:
         result["comparisons"] = comparisons(
@@ -269,6 +290,64 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_bits, ids_np, wgu_bits, S, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+_FLUSH = None
+
+
+def time_cold(fn, reps):
+    """Average µs of one launch of fn, each launch preceded (outside its events)
+    by a 512 MiB device write that evicts the last-level cache."""
+    import torch
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for _ in range(2):
+        _FLUSH.fill_(1.0)
+        fn()
+    for st, en in evs:
+        _FLUSH.fill_(1.0)
+        st.record(stream)
+        fn()
+        en.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([st.elapsed_time(en) for st, en in evs])) * 1e3
+
+
+def gate_up_by_routing(step_routing, step_us, t, reps):
+    """The gate_up GEMM under the three routings of the same tokens (softmax
+    top-8, uniform 8-subsets, Zipf(1.2)), each timed over `reps` launches after
+    the timed steps, on the step's weights and output buffer."""
+    import torch
+    import precision_moe_gemm_amd as pmg
+    import workloads as W
+    T, E, k, I, H, x = t["T"], t["E"], t["k"], t["I"], t["H"], t["x"]
+    out = {f"{step_routing}_in_step": {"us": round(step_us, 2)}}
+    for kind in ("softmax", "uniform", "zipf"):
+        ids_np, _ = W.make_routing(kind, T, E, k, t["cfg"])
+        perm = pmg.nvfp4_quantize_permute(x, torch.from_numpy(ids_np).to(x.device), E, workspace=t["ws"])
+        off = perm["expert_offsets"]
+        out[kind] = {"us": round(_time_op(lambda: pmg.nvfp4_grouped_gemm(
+            perm["codes"], perm["bscales"], perm["rscales"], off, *t["q_gu"], c=t["gu"]), reps), 2)}
+        del perm
+    for kind, d in out.items():
+        tf = 2.0 * T * k * H * 2 * I / (d["us"] * 1e-6) / 1e12
+        d.update(TFLOPs=round(tf, 1), frac_f16_mfma_peak=round(tf / PEAK_F16_TFLOPS, 4))
+    out["how"] = (f"{step_routing}_in_step: the timed steps' figure; per routing: 3 untimed + {reps} timed "
+                  "back-to-back launches after the steps, same weights and output buffer")
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 def graph_steps(step, steps, warmup, T):
@@ -445,7 +524,7 @@ def cpu_baseline(x_bits, ids, wgu_bits, S, budget_s):
             "sample": f"oracle gate_up grouped GEMM over the routed rows of experts 0..{e - 1} "
                       f"({int(off[e] - off[0])} of {Rr} rows); oracle quantize-permute of all {S.T} tokens",
             "quantize_permute_GBps": round(qp_bytes / qp_s / 1e9, 4),
-            "cpu": platform.processor() or platform.machine(), "seconds": round(g_s + qp_s, 2)}
+            "cpu": cpu_model(), "seconds": round(g_s + qp_s, 2)}
 
 
 if __name__ == "__main__":

@@ -57,7 +57,7 @@ extern "C" {
 #endif
 
 #define NVFP4MOE_API __attribute__((visibility("default")))
-#define NVFP4MOE_ABI_VERSION 1
+#define NVFP4MOE_ABI_VERSION 2
 #define NVFP4MOE_MAX_K 8192      /* longest quantised row */
 #define NVFP4MOE_MAX_EXPERTS 1024
 #define NVFP4MOE_MAX_TOPK 32
@@ -82,8 +82,47 @@ NVFP4MOE_API const char* nvfp4moe_status_string(int status);
 /* NVFP4MOE_ABI_VERSION of the built library. */
 NVFP4MOE_API int nvfp4moe_abi_version(void);
 
-/* Bytes of device workspace nvfp4_quantize_permute needs for T tokens, top-k, E experts. */
+/* Bytes of device workspace nvfp4_quantize_permute needs for T tokens, top-k, E experts
+ * (0 for invalid sizes). */
 NVFP4MOE_API size_t nvfp4moe_permute_workspace_size(int64_t T, int32_t k, int32_t E);
+
+/*
+ * nvfp4moe_workspace_size - device workspace bytes an operation needs, keyed by
+ * the operation.  Only the route + permute + quantise pass uses a workspace
+ * (its per-(chunk, expert) count table and one rank per routing entry); every
+ * other operation enqueues kernels on caller buffers alone and returns 0.
+ *   op     NVFP4MOE_OP_* below
+ *   T, E, k: tokens, experts, top-k of the routing (NVFP4MOE_OP_QUANTIZE_PERMUTE)
+ *   R_max, N: routed-row capacity and output width (GEMMs; unused, 0 is returned)
+ * Returns (size_t)-1 for an unknown op, 0 where no workspace is needed or the
+ * sizes are invalid.
+ */
+#define NVFP4MOE_OP_QUANTIZE_PERMUTE 0
+#define NVFP4MOE_OP_QUANTIZE_ROWS 1
+#define NVFP4MOE_OP_GROUPED_GEMM 2
+#define NVFP4MOE_OP_SWIGLU_QUANTIZE 3
+#define NVFP4MOE_OP_UNPERMUTE_COMBINE 4
+#define NVFP4MOE_OP_BF16_GROUPED_GEMM 5
+#define NVFP4MOE_OP_SWIGLU_BACKWARD 6
+NVFP4MOE_API size_t nvfp4moe_workspace_size(int32_t op, int64_t T, int32_t E, int32_t k,
+                                            int64_t R_max, int64_t N);
+
+/*
+ * Byte offsets of a row's NVFP4 block scale and element code in the two
+ * storage layouts (host functions, no device access).  The "scale-layout
+ * conversion fused into quantisation" of the blog "miniTE NVFP4" (section "Two
+ * complementary interventions") is the quantiser writing the layout the GEMM
+ * reads; these functions name where each byte of that layout lives.
+ *   group_rows = 0: row-major, bscales [rows][K/16], codes [rows][K/2];
+ *   group_rows = G > 0: K-tiled groups of G rows (nvfp4_quantize_rows_tiled),
+ *     bscales [rows/G][K/64][G][4], codes [rows/G][K/64][G][32].
+ * nvfp4moe_bscale_index: the byte of block kb (elements 16 kb .. 16 kb + 15) of
+ * row r.  nvfp4moe_code_index: the byte holding element i of row r (low nibble
+ * for even i, high nibble for odd i).  Requires K % 16 == 0 (row-major) or
+ * K % 64 == 0 (K-tiled), 0 <= kb < K/16, 0 <= i < K, r >= 0; returns -1 otherwise.
+ */
+NVFP4MOE_API int64_t nvfp4moe_bscale_index(int64_t r, int64_t kb, int64_t K, int64_t group_rows);
+NVFP4MOE_API int64_t nvfp4moe_code_index(int64_t r, int64_t i, int64_t K, int64_t group_rows);
 
 /*
  * nvfp4_quantize_rows - NVFP4-quantise `rows` bf16 rows of length K, each with
@@ -178,19 +217,28 @@ NVFP4MOE_API int nvfp4_quantize_permute_noalloc(const uint16_t* x, int64_t T, in
  *   W (weights), w_layout NVFP4_W_ROWMAJOR: w_codes [E][N][K/2], w_bscales [E][N][K/16];
  *                w_layout NVFP4_W_KTILED:   w_codes [E][K/64][N][32], w_bscales [E][K/64][N][4]
  *                (nvfp4_quantize_rows_tiled with group_rows = N); w_rscales [E][N]
- *   c                float [R_cap][N]; only rows < expert_offsets[E] are written
- * E = 1 with expert_offsets = {0, M} is a dense GEMM of M rows.
+ *   c                [R_cap][N] of c_dtype: NVFP4_OUT_F32 (float) or NVFP4_OUT_BF16
+ *                    (bf16 bits, each FP32 result rounded to nearest even; halves the
+ *                    output bytes, at 2^-9 relative error on top of the bound above);
+ *                    only rows < expert_offsets[E] are written
+ * E = 1 with expert_offsets = {0, M} is a dense GEMM of M rows.  The list of
+ * (expert, row block, column block) tiles is derived on the device from
+ * expert_offsets by every workgroup (no tile list argument).
+ * expert_offsets must be non-decreasing with expert_offsets[E] <= R_cap (as
+ * nvfp4_quantize_permute writes them).
  * Requires K % 64 == 0, N % 16 == 0, 16 <= N <= 2^20, K <= 65536, all pointers
- * 16-byte aligned.  Unknown w_layout: NVFP4_ERR_ARG.
+ * 16-byte aligned.  Unknown w_layout or c_dtype: NVFP4_ERR_ARG.
  */
 #define NVFP4_W_ROWMAJOR 0
 #define NVFP4_W_KTILED 1
+#define NVFP4_OUT_F32 0
+#define NVFP4_OUT_BF16 1
 NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_bscales,
                                     const float* a_rscales, const int32_t* expert_offsets,
                                     int32_t E, int64_t R_cap, const uint8_t* w_codes,
                                     const uint8_t* w_bscales, const float* w_rscales,
-                                    int64_t N, int64_t K, int32_t w_layout, float* c,
-                                    void* stream);
+                                    int64_t N, int64_t K, int32_t w_layout, void* c,
+                                    int32_t c_dtype, void* stream);
 
 /*
  * swiglu_quantize - weighted SwiGLU of the gate_up output with the amax taken

@@ -26,6 +26,10 @@ W_KN = 0
 W_NK = 1
 W_ROWMAJOR = 0   # NVFP4 weights [E, N, K/2] / [E, N, K/16]
 W_KTILED = 1     # NVFP4 weights [E, K/64, N, 32] / [E, K/64, N, 4]
+OUT_F32 = 0      # grouped GEMM output dtypes
+OUT_BF16 = 1
+OP_QUANTIZE_PERMUTE, OP_QUANTIZE_ROWS, OP_GROUPED_GEMM, OP_SWIGLU_QUANTIZE = 0, 1, 2, 3
+OP_UNPERMUTE_COMBINE, OP_BF16_GROUPED_GEMM, OP_SWIGLU_BACKWARD = 4, 5, 6
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -52,13 +56,16 @@ SIGNATURES = {
     "nvfp4moe_status_string": ([_I32], _c.c_char_p),
     "nvfp4moe_abi_version": ([], _c.c_int),
     "nvfp4moe_permute_workspace_size": ([_I64, _I32, _I32], _c.c_size_t),
+    "nvfp4moe_workspace_size": ([_I32, _I64, _I32, _I32, _I64, _I64], _c.c_size_t),
+    "nvfp4moe_bscale_index": ([_I64, _I64, _I64, _I64], _I64),
+    "nvfp4moe_code_index": ([_I64, _I64, _I64, _I64], _I64),
     "nvfp4_quantize_rows": ([_P, _I64, _I64, _P, _P, _P, _P], _c.c_int),
     "nvfp4_quantize_permute": ([_P, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                                 _c.c_size_t, _P, _P], _c.c_int),
     "nvfp4_quantize_permute_noalloc": ([_P, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P],
                                        _c.c_int),
     "nvfp4_quantize_rows_tiled": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], _c.c_int),
-    "nvfp4_grouped_gemm": ([_P, _P, _P, _P, _I32, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _P],
+    "nvfp4_grouped_gemm": ([_P, _P, _P, _P, _I32, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _I32, _P],
                            _c.c_int),
     "swiglu_quantize": ([_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P, _P], _c.c_int),
     "unpermute_combine": ([_P, _I64, _I32, _I64, _P, _P, _P, _P], _c.c_int),
@@ -173,6 +180,21 @@ def permute_workspace_size(T: int, k: int, E: int) -> int:
     return int(load_library().nvfp4moe_permute_workspace_size(T, k, E))
 
 
+def workspace_size(op: int, T: int = 0, E: int = 0, k: int = 0, R_max: int = 0, N: int = 0) -> int:
+    """Device workspace bytes of an operation (OP_*); only OP_QUANTIZE_PERMUTE needs any."""
+    return int(load_library().nvfp4moe_workspace_size(op, T, E, k, R_max, N))
+
+
+def bscale_index(r: int, kb: int, K: int, group_rows: int = 0) -> int:
+    """Byte offset of block kb of row r: row-major (group_rows 0) or K-tiled groups."""
+    return int(load_library().nvfp4moe_bscale_index(r, kb, K, group_rows))
+
+
+def code_index(r: int, i: int, K: int, group_rows: int = 0) -> int:
+    """Byte offset of the byte holding element i of row r (low nibble for even i)."""
+    return int(load_library().nvfp4moe_code_index(r, i, K, group_rows))
+
+
 def nvfp4_quantize_permute(x, topk_ids, E: int, workspace=None, dev_err=None, out=None):
     """Route + permute + quantise.  Returns dict with codes, bscales, rscales,
     expert_offsets [E+1], row_to_tk [T*k], tk_to_row [T*k]."""
@@ -237,8 +259,9 @@ def nvfp4_quantize_permute_noalloc(x, topk_ids, E: int, out, dev_err=None):
 
 
 def nvfp4_grouped_gemm(a_codes, a_bscales, a_rscales, expert_offsets, w_codes, w_bscales,
-                       w_rscales, c=None):
-    """C[r] = A[r] W_e^T over expert-grouped rows.  Returns C f32 [R_cap, N].
+                       w_rscales, c=None, out_dtype=None):
+    """C[r] = A[r] W_e^T over expert-grouped rows.  Returns C [R_cap, N], float32
+    (default) or bfloat16 (out_dtype=torch.bfloat16, or a bf16 `c`).
     W in either layout: row-major codes [E, N, K/2] (bscales [E, N, K/16]) or
     K-tiled codes [E, K/64, N, 32] (bscales [E, K/64, N, 4]); w_rscales [E, N]."""
     for t, n, d in ((a_codes, "a_codes", _U8), (a_bscales, "a_bscales", _U8),
@@ -261,11 +284,16 @@ def nvfp4_grouped_gemm(a_codes, a_bscales, a_rscales, expert_offsets, w_codes, w
     _req(a_bscales, "a_bscales", _U8, numel=R_cap * (K // 16))
     _req(a_rscales, "a_rscales", _F32, numel=R_cap)
     _req(w_rscales, "w_rscales", _F32, numel=E * N)
-    c = _empty((R_cap, N), torch.float32, a_codes) if c is None else c
-    _req(c, "c", _F32, numel=R_cap * N)
+    if out_dtype is None:
+        out_dtype = torch.float32 if c is None or c.dtype == torch.float32 else torch.bfloat16
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    c = _empty((R_cap, N), out_dtype, a_codes) if c is None else c
+    _req(c, "c", _F32 if out_dtype == torch.float32 else _BF16, numel=R_cap * N)
     _check("nvfp4_grouped_gemm", load_library().nvfp4_grouped_gemm(
         _ptr(a_codes), _ptr(a_bscales), _ptr(a_rscales), _ptr(expert_offsets), E, R_cap,
-        _ptr(w_codes), _ptr(w_bscales), _ptr(w_rscales), N, K, layout, _ptr(c), _stream()))
+        _ptr(w_codes), _ptr(w_bscales), _ptr(w_rscales), N, K, layout, _ptr(c),
+        OUT_F32 if out_dtype == torch.float32 else OUT_BF16, _stream()))
     return c
 
 

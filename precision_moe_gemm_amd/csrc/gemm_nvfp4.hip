@@ -205,13 +205,14 @@ __device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_star
   return t;
 }
 
-template <bool KT>
+// KT: K-tiled weights; OB: BF16 output (each FP32 result rounded to nearest even)
+template <bool KT, bool OB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_bscales,
     const float* __restrict__ a_rscales, const int32_t* __restrict__ offsets, int E,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_bscales,
-    const float* __restrict__ w_rscales, int N, int K, float* __restrict__ c) {
+    const float* __restrict__ w_rscales, int N, int K, void* __restrict__ c) {
   __shared__ Smem sm;
   constexpr bool w_tiled = KT;
 
@@ -517,8 +518,47 @@ void grouped_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < FA; ++i) sa[i] = rs_a[32 * i + l32];
     uint8_t* stg = sm.stg[wave];
+    constexpr int kOutB = OB ? 2 : 4;             // bytes per output element
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        c + (int64_t)t.m0 * N, (short)0, t.rows * N * 4, 0x00020000);
+        static_cast<uint8_t*>(c) + (int64_t)t.m0 * N * kOutB, (short)0, t.rows * N * kOutB, 0x00020000);
+    if constexpr (OB) {
+      // BF16: a 32 x 32 tile is 32 rows of 64 bytes; each store instruction
+      // writes 16 rows (4 lanes x 16 bytes per row).  Staging: row l32, 8-byte
+      // piece 2q + h, the row's four 16-byte chunks XOR-swizzled by row.
+      const int srow = lane >> 2, sch = lane & 3;
+      uint32_t srowN = (uint32_t)(srow * N);
+      asm volatile("" : "+v"(srowN));
+#pragma unroll
+      for (int j = 0; j < FB; ++j) {
+        float4 swv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          swv[q] = *reinterpret_cast<const float4*>(&rs_w[WN * wave + 32 * j + 8 * q + 4 * h]);
+        const int n = t.n0 + WN * wave + 32 * j + 8 * sch;
+#pragma unroll
+        for (int i = 0; i < FA; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float o0 = (acc[i][j][4 * q + 0] * sa[i]) * swv[q].x;
+            const float o1 = (acc[i][j][4 * q + 1] * sa[i]) * swv[q].y;
+            const float o2 = (acc[i][j][4 * q + 2] * sa[i]) * swv[q].z;
+            const float o3 = (acc[i][j][4 * q + 3] * sa[i]) * swv[q].w;
+            const uint2 pk = make_uint2(f32_to_bf16_rne(o0) | (f32_to_bf16_rne(o1) << 16),
+                                        f32_to_bf16_rne(o2) | (f32_to_bf16_rne(o3) << 16));
+            *reinterpret_cast<uint2*>(stg + l32 * 64 + ((q ^ (l32 & 3)) << 4) + 8 * h) = pk;
+          }
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int row = 16 * r + srow;
+            const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 64 + ((sch ^ (row & 3)) << 4));
+            const uint32_t off = n < N ? ((uint32_t)((32 * i + 16 * r) * N) + srowN + (uint32_t)n) * 2u : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rsrc, off, 0, kNonTemporal);
+          }
+          acc[i][j] = floatx16{};
+        }
+      }
+      return;
+    }
     const int srow = lane >> 3, sch = lane & 7;   // store layout: 8 rows x 8 chunks per instruction
     // the lane's row offset, recomputed per tile: kept opaque so that the
     // compiler does not hoist sixteen per-lane row offsets out of the tile loop
@@ -609,9 +649,10 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uin
                                                const int32_t* expert_offsets, int32_t E,
                                                int64_t R_cap, const uint8_t* w_codes,
                                                const uint8_t* w_bscales, const float* w_rscales,
-                                               int64_t N, int64_t K, int32_t w_layout, float* c,
-                                               void* stream) {
+                                               int64_t N, int64_t K, int32_t w_layout, void* c,
+                                               int32_t c_dtype, void* stream) {
   if (w_layout != NVFP4_W_ROWMAJOR && w_layout != NVFP4_W_KTILED) return NVFP4_ERR_ARG;
+  if (c_dtype != NVFP4_OUT_F32 && c_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_ARG;
   if (E < 1 || E > NVFP4MOE_MAX_EXPERTS || R_cap < 0) return NVFP4_ERR_SHAPE;
   if (K <= 0 || K % g5::BK != 0 || K > 65536 || N < 16 || N % 16 != 0 || N > (1 << 20))
     return NVFP4_ERR_SHAPE;
@@ -633,13 +674,15 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uin
   int64_t grid = max_tiles < 256 ? max_tiles : 256;
   if (grid >= 8) grid &= ~7ll;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (w_layout == NVFP4_W_KTILED)
-    g5::grouped_gemm_kernel<true><<<(unsigned)grid, g5::kThreads, 0, s>>>(
-        a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales, (int)N,
-        (int)K, c);
-  else
-    g5::grouped_gemm_kernel<false><<<(unsigned)grid, g5::kThreads, 0, s>>>(
-        a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales, (int)N,
-        (int)K, c);
+#define GG_LAUNCH(KT, OB)                                                                    \
+  g5::grouped_gemm_kernel<KT, OB><<<(unsigned)grid, g5::kThreads, 0, s>>>(                    \
+      a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales, (int)N, \
+      (int)K, c)
+  const bool kt = w_layout == NVFP4_W_KTILED, ob = c_dtype == NVFP4_OUT_BF16;
+  if (kt && !ob) GG_LAUNCH(true, false);
+  else if (kt) GG_LAUNCH(true, true);
+  else if (!ob) GG_LAUNCH(false, false);
+  else GG_LAUNCH(false, true);
+#undef GG_LAUNCH
   return launch_status();
 }

@@ -770,12 +770,44 @@ NVFP4MOE_API const char* nvfp4moe_status_string(int status) {
 
 NVFP4MOE_API int nvfp4moe_abi_version(void) { return NVFP4MOE_ABI_VERSION; }
 
+NVFP4MOE_API int64_t nvfp4moe_bscale_index(int64_t r, int64_t kb, int64_t K, int64_t group_rows) {
+  if (r < 0 || K <= 0 || kb < 0 || kb >= K / 16 || group_rows < 0) return -1;
+  if (group_rows == 0) return K % 16 ? -1 : r * (K / 16) + kb;
+  if (K % 64) return -1;
+  const int64_t g = r / group_rows, rr = r - g * group_rows;
+  return ((g * (K / 64) + kb / 4) * group_rows + rr) * 4 + kb % 4;
+}
+
+NVFP4MOE_API int64_t nvfp4moe_code_index(int64_t r, int64_t i, int64_t K, int64_t group_rows) {
+  if (r < 0 || K <= 0 || i < 0 || i >= K || group_rows < 0) return -1;
+  if (group_rows == 0) return K % 16 ? -1 : r * (K / 2) + i / 2;
+  if (K % 64) return -1;
+  const int64_t g = r / group_rows, rr = r - g * group_rows;
+  return ((g * (K / 64) + i / 64) * group_rows + rr) * 32 + (i % 64) / 2;
+}
+
 NVFP4MOE_API size_t nvfp4moe_permute_workspace_size(int64_t T, int32_t k, int32_t E) {
   if (T < 0 || k <= 0 || E <= 0) return 0;
   // the (chunk, expert) count table and a rank per routing entry
   const int64_t n = T * (int64_t)k;
   const size_t bytes = ((size_t)plan_chunks(n) * (size_t)E + (size_t)n) * sizeof(int32_t);
   return (bytes + 255) & ~(size_t)255;
+}
+
+NVFP4MOE_API size_t nvfp4moe_workspace_size(int32_t op, int64_t T, int32_t E, int32_t k,
+                                            int64_t R_max, int64_t N) {
+  (void)R_max;
+  (void)N;
+  switch (op) {
+    case NVFP4MOE_OP_QUANTIZE_PERMUTE: return nvfp4moe_permute_workspace_size(T, k, E);
+    case NVFP4MOE_OP_QUANTIZE_ROWS:
+    case NVFP4MOE_OP_GROUPED_GEMM:
+    case NVFP4MOE_OP_SWIGLU_QUANTIZE:
+    case NVFP4MOE_OP_UNPERMUTE_COMBINE:
+    case NVFP4MOE_OP_BF16_GROUPED_GEMM:
+    case NVFP4MOE_OP_SWIGLU_BACKWARD: return 0;
+    default: return (size_t)-1;
+  }
 }
 
 NVFP4MOE_API int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t K, uint8_t* codes,

@@ -58,12 +58,27 @@ def quantize_weights_gpu_tiled(w_bits: np.ndarray):
 
 
 def ktile(codes: np.ndarray, bscales: np.ndarray):
-    """Row-major NVFP4 [G, R, K/2] / [G, R, K/16] -> the K-tiled layout
-    [G, K/64, R, 32] / [G, K/64, R, 4] (a pure move of bytes)."""
-    G, R, half = codes.shape
-    kt = half // 32
-    return (codes.reshape(G, R, kt, 32).transpose(0, 2, 1, 3).copy(),
-            bscales.reshape(G, R, kt, 4).transpose(0, 2, 1, 3).copy())
+    """Row-major NVFP4 [groups, G, K/2] / [groups, G, K/16] -> the K-tiled layout
+    [groups, K/64, G, 32] / [groups, K/64, G, 4], each byte moved to the offset the
+    library's nvfp4moe_code_index / nvfp4moe_bscale_index name for it.  The
+    offsets of one group come from those functions (one call per byte); a later
+    group's are the first group's plus the group's size, which is checked on
+    the last group's first and last rows."""
+    n_grp, G, half = codes.shape
+    K = half * 2
+    ci = np.array([[pmg.code_index(r, 2 * b, K, G) for b in range(half)] for r in range(G)], np.int64)
+    si = np.array([[pmg.bscale_index(r, kb, K, G) for kb in range(K // 16)] for r in range(G)], np.int64)
+    last = (n_grp - 1) * G
+    for r in (0, G - 1):
+        assert [pmg.code_index(last + r, 2 * b, K, G) for b in (0, half - 1)] == \
+            [int(ci[r, 0]) + last * half, int(ci[r, -1]) + last * half]
+        assert pmg.bscale_index(last + r, K // 16 - 1, K, G) == int(si[r, -1]) + last * (K // 16)
+    out_c = np.empty(codes.size, np.uint8)
+    out_s = np.empty(bscales.size, np.uint8)
+    g_off = np.arange(n_grp, dtype=np.int64)[:, None, None]
+    out_c[(ci[None] + g_off * G * half).reshape(-1)] = codes.reshape(-1)
+    out_s[(si[None] + g_off * G * (K // 16)).reshape(-1)] = bscales.reshape(-1)
+    return (out_c.reshape(n_grp, K // 64, G, 32), out_s.reshape(n_grp, K // 64, G, 4))
 
 
 def assert_within(got: np.ndarray, ref: np.ndarray, bound: np.ndarray, what: str = ""):

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.nvfp4moe_abi_version() == 1
+    assert lib.nvfp4moe_abi_version() == 2
     for s in range(8):
         assert pmg.status_string(s) and pmg.status_string(s) != pmg.status_string(99)
     assert "unknown" in pmg.status_string(99)
@@ -93,7 +93,8 @@ def test_gemm_host_checks(lib):
     base = dict(E=128, R=32768, N=1536, K=2048)
     call = lambda **kw: f(FAKE, FAKE, FAKE, FAKE, kw.get("E", 128), kw.get("R", 32768), FAKE, FAKE,
                           kw.get("wr", FAKE), kw.get("N", 1536), kw.get("K", 2048), kw.get("lay", 0),
-                          kw.get("c", FAKE), None)
+                          kw.get("c", FAKE), kw.get("cd", 0), None)
+    assert call(cd=2) == ERR_ARG                            # unknown output dtype
     assert call(K=2000) == ERR_SHAPE                        # K % 64
     assert call(N=(1 << 20) + 16) == ERR_SHAPE
     assert call(lay=2) == ERR_ARG
@@ -157,3 +158,36 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(pmg, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(pmg.LibraryNotBuilt):
         pmg.load_library()
+
+
+def test_workspace_size_by_op(lib):
+    T, k, E = 4096, 8, 128
+    assert pmg.workspace_size(pmg.OP_QUANTIZE_PERMUTE, T=T, E=E, k=k) == lib.nvfp4moe_permute_workspace_size(T, k, E)
+    for op in (pmg.OP_QUANTIZE_ROWS, pmg.OP_GROUPED_GEMM, pmg.OP_SWIGLU_QUANTIZE, pmg.OP_UNPERMUTE_COMBINE,
+               pmg.OP_BF16_GROUPED_GEMM, pmg.OP_SWIGLU_BACKWARD):
+        assert pmg.workspace_size(op, T=T, E=E, k=k, R_max=T * k, N=1536) == 0
+    assert pmg.workspace_size(99) == 2 ** 64 - 1
+
+
+def test_scale_and_code_indices_match_the_layouts():
+    """The exported index functions against the layouts stated in the header: the
+    row-major layout is [rows][K/16] / [rows][K/2]; the K-tiled layout moves the
+    same bytes to [rows/G][K/64][G][4] / [rows/G][K/64][G][32].  Built here by
+    numpy reshapes of an array of byte labels, independent of the C functions."""
+    import numpy as np
+    for rows, K, G in [(6, 128, 3), (8, 64, 8), (4, 192, 1)]:
+        lab_s = np.arange(rows * K // 16).reshape(rows, K // 16)        # row-major: label = offset
+        lab_c = np.arange(rows * K // 2).reshape(rows, K // 2)
+        til_s = lab_s.reshape(rows // G, G, K // 64, 4).transpose(0, 2, 1, 3).reshape(-1)
+        til_c = lab_c.reshape(rows // G, G, K // 64, 32).transpose(0, 2, 1, 3).reshape(-1)
+        pos_s = np.empty_like(til_s); pos_s[til_s] = np.arange(til_s.size)   # label -> K-tiled offset
+        pos_c = np.empty_like(til_c); pos_c[til_c] = np.arange(til_c.size)
+        for r in range(rows):
+            for kb in range(K // 16):
+                assert pmg.bscale_index(r, kb, K) == lab_s[r, kb]
+                assert pmg.bscale_index(r, kb, K, G) == pos_s[lab_s[r, kb]]
+            for i in range(K):
+                assert pmg.code_index(r, i, K) == lab_c[r, i // 2]
+                assert pmg.code_index(r, i, K, G) == pos_c[lab_c[r, i // 2]]
+    assert pmg.bscale_index(0, 8, 128) == -1 and pmg.code_index(0, 128, 128) == -1
+    assert pmg.bscale_index(0, 0, 96, 4) == -1                         # K-tiled needs K % 64

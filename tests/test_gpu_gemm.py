@@ -42,10 +42,17 @@ def _routed_case(T, H, E, k, N, kind, seed):
     c = host(pmg.nvfp4_grouped_gemm(*a, *quantize_weights_gpu(w_bits)))
     # the K-tiled weight layout is the same computation on moved bytes
     (off, r2t, t2r), a_ref = ol.quantize_permute_ref(x, ids, E)
+    R = int(off[-1])
     if H % 64 == 0:
-        ct = host(pmg.nvfp4_grouped_gemm(*a, *quantize_weights_gpu_tiled(w_bits)))
-        R = int(off[-1])
+        wt = quantize_weights_gpu_tiled(w_bits)
+        ct = host(pmg.nvfp4_grouped_gemm(*a, *wt))
         assert np.array_equal(ct[:R], c[:R]), "K-tiled weights change the result"
+        # BF16 output: each FP32 result rounded to nearest even; rows past the routed ones untouched
+        cb = torch.full((T * k, N), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+        pmg.nvfp4_grouped_gemm(*a, *wt, c=cb)
+        cb_h = host(cb.view(torch.int16)).view(np.uint16)
+        assert np.array_equal(cb_h[:R], W.f32_to_bf16_bits(c[:R])), "BF16 output is not the rounded FP32 output"
+        assert np.all(cb_h[R:] == 0xFFFF)
     return c, off, a_ref, w_bits
 
 
