@@ -285,7 +285,8 @@ def main():
     result["practical_ceiling"] = practical_ceiling(gu_tf, per_op["quantize_permute"]["GBps"])
     if not args.no_comparisons:
         result["comparisons"] = comparisons(
-            dict(x=x, dy=dy, ids=ids, E=E, k=k, I=I, H=H, perm=perm, wgu=wgu, wd=wd, dgu=dgu, ws=ws),
+            dict(x=x, dy=dy, ids=ids, E=E, k=k, I=I, H=H, perm=perm, wgu=wgu, wd=wd, dgu=dgu, ws=ws,
+                 q_gu=q_gu, tw=tw, gu=gu, a2=a2),
             gemm_flops, op_ms)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_bits, ids_np, wgu_bits, S, args.cpu_seconds)
@@ -454,6 +455,25 @@ def comparisons(t, gemm_flops, op_ms):
         "dgrad_gate_up_gemm": {"us": round(us_dg, 2), "TFLOPs": tf("dgrad_gate_up_gemm", us_dg)},
         "total_us": round(total, 2), "bf16_dgrad_gemms_us": round(bf, 2),
         "speedup_vs_bf16": round(bf / total, 3)}
+    # the weighted SwiGLU fused into the gate_up GEMM's epilogue (FP32 SwiGLU), then the
+    # FP32-row quantiser, against gate_up GEMM + the float64 SwiGLU-quantise pass; once
+    # without the gate/up output (forward only) and once with it (kept for the backward)
+    h = torch.empty(R, I, dtype=torch.float32, device=dev)
+    fws = torch.empty(pmg.workspace_size(pmg.OP_GROUPED_GEMM_SWIGLU, R_max=R), dtype=torch.uint8, device=dev)
+    a = (perm["codes"], perm["bscales"], perm["rscales"], off)
+    a2 = t["a2"]
+    fused = lambda gu_out: pmg.nvfp4_grouped_gemm_swiglu(*a, *t["q_gu"], topk_w=t["tw"], row_to_tk=perm["row_to_tk"],
+                                                         h=h, gu=gu_out, workspace=fws)
+    us_f = _time_op(lambda: fused(None))
+    us_fg = _time_op(lambda: fused(t["gu"]))
+    us_q = _time_op(lambda: pmg.nvfp4_quantize_rows_f32(h, off, a2["codes"], a2["bscales"], a2["rscales"]))
+    sep = (op_ms["gate_up_gemm"] + op_ms["swiglu_quantize"]) * 1e3
+    out["fused_swiglu_gate_up"] = {
+        "gemm_swiglu_us": round(us_f, 2), "gemm_swiglu_with_gu_us": round(us_fg, 2),
+        "quantize_h_us": round(us_q, 2),
+        "separate_gemm_plus_swiglu_quantize_us": round(sep, 2),
+        "speedup_forward_only": round(sep / (us_f + us_q), 3),
+        "speedup_with_gu": round(sep / (us_fg + us_q), 3)}
     out["how"] = ("after the timed steps: 3 untimed + 10 timed launches per op, HIP events on the "
                   "launch stream; same routing, shapes and buffers as the step")
     return out

@@ -104,6 +104,7 @@ NVFP4MOE_API size_t nvfp4moe_permute_workspace_size(int64_t T, int32_t k, int32_
 #define NVFP4MOE_OP_UNPERMUTE_COMBINE 4
 #define NVFP4MOE_OP_BF16_GROUPED_GEMM 5
 #define NVFP4MOE_OP_SWIGLU_BACKWARD 6
+#define NVFP4MOE_OP_GROUPED_GEMM_SWIGLU 7   /* R_max * 4 bytes (router weight per row) */
 NVFP4MOE_API size_t nvfp4moe_workspace_size(int32_t op, int64_t T, int32_t E, int32_t k,
                                             int64_t R_max, int64_t N);
 
@@ -239,6 +240,48 @@ NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_bsc
                                     const uint8_t* w_bscales, const float* w_rscales,
                                     int64_t N, int64_t K, int32_t w_layout, void* c,
                                     int32_t c_dtype, void* stream);
+
+/*
+ * nvfp4_grouped_gemm_swiglu - the gate_up grouped GEMM with the weighted SwiGLU
+ * in its epilogue (the blog "miniTE NVFP4", section "Two complementary
+ * interventions", takes the amax during the weighted SwiGLU; here the SwiGLU
+ * itself moves into the GEMM that produces its input, so the gate_up output
+ * need not make a round trip through memory).  For every routed row r of
+ * expert e and h column j in [0, I):
+ *     g = C[r][j], u = C[r][I + j]  (C = A W_e^T as nvfp4_grouped_gemm computes it, FP32)
+ *     h[r][j] = (silu(g) * u) * w_r,  silu(g) = g / (1 + exp(-g)),  in FP32
+ * with w_r = topk_w[row_to_tk[r]] (1 when topk_w is NULL).  exp is the hardware
+ * exp2 of -g log2(e): h lies within 2^-20 |h64| + 2^-24 max_row |h64| of the
+ * float64 value h64 of the same g and u.  Quantise h with nvfp4_quantize_rows_f32
+ * (its amax is taken while it reads h).
+ *   A, expert_offsets, E, R_cap, K: as nvfp4_grouped_gemm
+ *   W: K-tiled only, w_codes [E][K/64][2I][32], w_bscales [E][K/64][2I][4],
+ *      w_rscales [E][2I]: gate rows [0, I), up rows [I, 2I)
+ *   h    float [R_cap][I]
+ *   gu   float [R_cap][2I] or NULL: the plain GEMM's output (bit-identical to
+ *        nvfp4_grouped_gemm's), for a backward pass that needs g and u
+ *   workspace: nvfp4moe_workspace_size(NVFP4MOE_OP_GROUPED_GEMM_SWIGLU, ..., R_max = R_cap, ...)
+ *        bytes when topk_w is given (may be NULL otherwise)
+ * Requires I % 256 == 0, 256 <= I <= 2^19, K % 64 == 0, K <= 65536.
+ */
+NVFP4MOE_API int nvfp4_grouped_gemm_swiglu(const uint8_t* a_codes, const uint8_t* a_bscales,
+                                           const float* a_rscales, const int32_t* expert_offsets,
+                                           int32_t E, int64_t R_cap, const uint8_t* w_codes,
+                                           const uint8_t* w_bscales, const float* w_rscales,
+                                           int64_t I, int64_t K, const float* topk_w,
+                                           const int32_t* row_to_tk, float* h, float* gu,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * nvfp4_quantize_rows_f32 - the NVFP4 row quantisation of FP32 rows (the
+ * definition at the top of this header, on FP32 inputs): rows
+ * [0, min(expert_offsets[E], rows)) when expert_offsets is given, else all rows.
+ *   x float [rows][K]; codes [rows][K/2]; bscales [rows][K/16]; rscales [rows]
+ * Requires K % 16 == 0, K <= NVFP4MOE_MAX_K.
+ */
+NVFP4MOE_API int nvfp4_quantize_rows_f32(const float* x, int64_t rows, int64_t K,
+                                         const int32_t* expert_offsets, int32_t E, uint8_t* codes,
+                                         uint8_t* bscales, float* rscales, void* stream);
 
 /*
  * swiglu_quantize - weighted SwiGLU of the gate_up output with the amax taken

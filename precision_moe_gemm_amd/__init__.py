@@ -29,7 +29,7 @@ W_KTILED = 1     # NVFP4 weights [E, K/64, N, 32] / [E, K/64, N, 4]
 OUT_F32 = 0      # grouped GEMM output dtypes
 OUT_BF16 = 1
 OP_QUANTIZE_PERMUTE, OP_QUANTIZE_ROWS, OP_GROUPED_GEMM, OP_SWIGLU_QUANTIZE = 0, 1, 2, 3
-OP_UNPERMUTE_COMBINE, OP_BF16_GROUPED_GEMM, OP_SWIGLU_BACKWARD = 4, 5, 6
+OP_UNPERMUTE_COMBINE, OP_BF16_GROUPED_GEMM, OP_SWIGLU_BACKWARD, OP_GROUPED_GEMM_SWIGLU = 4, 5, 6, 7
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -67,6 +67,9 @@ SIGNATURES = {
     "nvfp4_quantize_rows_tiled": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], _c.c_int),
     "nvfp4_grouped_gemm": ([_P, _P, _P, _P, _I32, _I64, _P, _P, _P, _I64, _I64, _I32, _P, _I32, _P],
                            _c.c_int),
+    "nvfp4_grouped_gemm_swiglu": ([_P, _P, _P, _P, _I32, _I64, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P,
+                                   _c.c_size_t, _P], _c.c_int),
+    "nvfp4_quantize_rows_f32": ([_P, _I64, _I64, _P, _I32, _P, _P, _P, _P], _c.c_int),
     "swiglu_quantize": ([_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P, _P], _c.c_int),
     "unpermute_combine": ([_P, _I64, _I32, _I64, _P, _P, _P, _P], _c.c_int),
     "permute_gather_bf16": ([_P, _I64, _I64, _I32, _P, _I32, _P, _P, _P], _c.c_int),
@@ -295,6 +298,66 @@ def nvfp4_grouped_gemm(a_codes, a_bscales, a_rscales, expert_offsets, w_codes, w
         _ptr(w_codes), _ptr(w_bscales), _ptr(w_rscales), N, K, layout, _ptr(c),
         OUT_F32 if out_dtype == torch.float32 else OUT_BF16, _stream()))
     return c
+
+
+def nvfp4_grouped_gemm_swiglu(a_codes, a_bscales, a_rscales, expert_offsets, w_codes, w_bscales,
+                              w_rscales, topk_w=None, row_to_tk=None, h=None, gu=None, want_gu=False,
+                              workspace=None):
+    """gate_up GEMM with the weighted SwiGLU in its epilogue.  W K-tiled
+    (codes [E, K/64, 2I, 32], bscales [E, K/64, 2I, 4], rscales [E, 2I]).
+    Returns (h f32 [R_cap, I], gu f32 [R_cap, 2I] or None)."""
+    for t, n, d in ((a_codes, "a_codes", _U8), (a_bscales, "a_bscales", _U8),
+                    (a_rscales, "a_rscales", _F32), (expert_offsets, "expert_offsets", _I32T),
+                    (w_codes, "w_codes", _U8), (w_bscales, "w_bscales", _U8),
+                    (w_rscales, "w_rscales", _F32), (topk_w, "topk_w", _F32), (row_to_tk, "row_to_tk", _I32T)):
+        _req(t, n, d)
+    R_cap = a_codes.shape[0]
+    K = a_codes.shape[1] * 2
+    E = expert_offsets.numel() - 1
+    if w_codes.dim() != 4 or w_codes.shape[0] != E or w_codes.shape[1] != K // 64 or w_codes.shape[2] % 2:
+        raise ValueError("w_codes must be K-tiled [E, K/64, 2I, 32]")
+    N = w_codes.shape[2]
+    I = N // 2
+    if tuple(w_bscales.shape) != (E, K // 64, N, 4):
+        raise ValueError("w_bscales must be K-tiled [E, K/64, 2I, 4]")
+    _req(a_bscales, "a_bscales", _U8, numel=R_cap * (K // 16))
+    _req(a_rscales, "a_rscales", _F32, numel=R_cap)
+    _req(w_rscales, "w_rscales", _F32, numel=E * N)
+    if topk_w is not None:
+        if row_to_tk is None:
+            raise ValueError("topk_w needs row_to_tk")
+        _req(topk_w, "topk_w", _F32, numel=R_cap)
+        _req(row_to_tk, "row_to_tk", _I32T, numel=R_cap)
+        ws_bytes = workspace_size(OP_GROUPED_GEMM_SWIGLU, R_max=R_cap)
+        workspace = _empty((ws_bytes,), torch.uint8, a_codes) if workspace is None else workspace
+        _req(workspace, "workspace", _U8, numel=ws_bytes)
+    h = _empty((R_cap, I), torch.float32, a_codes) if h is None else h
+    _req(h, "h", _F32, numel=R_cap * I)
+    if want_gu and gu is None:
+        gu = _empty((R_cap, N), torch.float32, a_codes)
+    _req(gu, "gu", _F32, numel=R_cap * N)
+    _check("nvfp4_grouped_gemm_swiglu", load_library().nvfp4_grouped_gemm_swiglu(
+        _ptr(a_codes), _ptr(a_bscales), _ptr(a_rscales), _ptr(expert_offsets), E, R_cap, _ptr(w_codes),
+        _ptr(w_bscales), _ptr(w_rscales), I, K, _ptr(topk_w), _ptr(row_to_tk), _ptr(h), _ptr(gu),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream()))
+    return h, gu
+
+
+def nvfp4_quantize_rows_f32(x, expert_offsets=None, codes=None, bscales=None, rscales=None):
+    """FP32 rows [rows, K] -> NVFP4 (codes, bscales, rscales); with expert_offsets only
+    the routed rows [0, offsets[E]) are written."""
+    _req(x, "x", _F32, 2)
+    _req(expert_offsets, "expert_offsets", _I32T)
+    rows, K = x.shape
+    E = 0 if expert_offsets is None else expert_offsets.numel() - 1
+    codes = _empty((rows, K // 2), torch.uint8, x) if codes is None else codes
+    bscales = _empty((rows, K // 16), torch.uint8, x) if bscales is None else bscales
+    rscales = _empty((rows,), torch.float32, x) if rscales is None else rscales
+    _req(codes, "codes", _U8, numel=rows * (K // 2)); _req(bscales, "bscales", _U8, numel=rows * (K // 16))
+    _req(rscales, "rscales", _F32, numel=rows)
+    _check("nvfp4_quantize_rows_f32", load_library().nvfp4_quantize_rows_f32(
+        _ptr(x), rows, K, _ptr(expert_offsets), E, _ptr(codes), _ptr(bscales), _ptr(rscales), _stream()))
+    return codes, bscales, rscales
 
 
 def swiglu_quantize(gu, expert_offsets, topk_w=None, row_to_tk=None, h_out=False, out=None):

@@ -96,6 +96,7 @@ struct __align__(16) Smem {
   uint8_t a16[2][BM * kA16Row];   // 2 x 16 KiB decoded activations (FP16)
   uint8_t stg[kWaves][4096];      // per-wavefront staging of one 32 x 32 FP32 output tile
   float rs[2][BM + BN];            // row scales of a tile's rows, then of its weight rows (epilogue)
+  float rw[2][BM];                 // router weights of a tile's rows (SwiGLU epilogue)
   int tile_start[NVFP4MOE_MAX_EXPERTS + 1];   // m-tiles before expert e
   int16_t mt_expert[kMtCap];                  // expert of m-tile tm (when they fit)
 };
@@ -205,14 +206,33 @@ __device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_star
   return t;
 }
 
-// KT: K-tiled weights; OB: BF16 output (each FP32 result rounded to nearest even)
-template <bool KT, bool OB>
+// Weighted SwiGLU of one gate/up pair in FP32: h = (silu(g) * u) * w, with
+// silu(g) = g / (1 + exp(-g)) (hardware exp2 of -g log2(e), correctly rounded
+// division).  Within a few FP32 ulps of the float64 value wherever |h| is not
+// negligible next to the row's largest |h| (for g far below zero exp(-g)
+// carries a relative error of about |g| 2^-24, while silu(g) is tiny).
+__device__ __forceinline__ float swiglu_f32(float g, float u, float w) {
+  const float e = __expf(-g);
+  return ((g / (1.0f + e)) * u) * w;
+}
+
+// KT: K-tiled weights; OB: BF16 output (each FP32 result rounded to nearest
+// even); SW: the weighted SwiGLU epilogue of the gate_up GEMM (K-tiled weights
+// [E][K/64][2I][32], gate rows [0, I), up rows [I, 2I); output h [R][I] FP32;
+// optionally gu [R][2I] FP32, the values the plain GEMM would write).  For SW
+// a tile covers h columns [256 tn, 256 tn + 256): wavefront w's column
+// fragment 0 holds gate rows 256 tn + 32 w + (0..31) and fragment 1 the up rows
+// I + 256 tn + 32 w + (0..31), so a lane holds g and u of the same (row,
+// column) in acc[i][0] and acc[i][1].
+template <bool KT, bool OB, bool SW>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_bscales,
     const float* __restrict__ a_rscales, const int32_t* __restrict__ offsets, int E,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_bscales,
-    const float* __restrict__ w_rscales, int N, int K, void* __restrict__ c) {
+    const float* __restrict__ w_rscales, int N, int K, void* __restrict__ c,
+    const float* __restrict__ w_rows, float* __restrict__ gu_out, int I) {
+  static_assert(!SW || (KT && !OB), "the SwiGLU epilogue reads K-tiled weights and writes FP32");
   __shared__ Smem sm;
   constexpr bool w_tiled = KT;
 
@@ -239,7 +259,7 @@ void grouped_gemm_kernel(
   }
   __syncthreads();
 
-  const int n_tiles = (N + BN - 1) / BN;
+  const int n_tiles = SW ? I / (BN / 2) : (N + BN - 1) / BN;
   const int total_m = __builtin_amdgcn_readfirstlane(sm.tile_start[E]);
   const int total = total_m * n_tiles;
   // each tile's expert by one LDS read instead of a binary search
@@ -304,6 +324,13 @@ void grouped_gemm_kernel(
                         : wave < 6 ? (uint32_t)offsetof(Stage, ws) + (uint32_t)(wave - 4) * 1024u
                                    : (uint32_t)offsetof(Stage, as) + (uint32_t)(wave - 6) * 256u;
   uint32_t vo0 = 0, vo1 = 0, vo2 = 0;
+  // weight row of tile column c (callers pass c with c % 4 == 0 or a whole
+  // 32-column group, so 4 consecutive columns map to 4 consecutive rows);
+  // plain tiles: row n0 + c, kept inside the weight matrix by `cap`
+  auto wcol = [&](const Tile& t, int c, int cap) __attribute__((always_inline)) -> int {
+    if constexpr (SW) return ((c >> 5) & 1) * I + (t.n0 >> 1) + ((c >> 6) << 5) + (c & 31);
+    else return min(t.n0 + c, cap);
+  };
   auto set_load_tile = [&](int L) __attribute__((always_inline)) {
     const Tile t = tile_at(L, n_tiles, sm.tile_start, mt_tab, E, offsets);
     if constexpr (KT) {
@@ -311,13 +338,13 @@ void grouped_gemm_kernel(
       const uint32_t half16 = (lane & 1) * 16;
       const uint32_t wbase = (uint32_t)t.e * nk * N;
       auto wrow = [&](int q) __attribute__((always_inline)) {
-        const uint32_t n = (uint32_t)min(t.n0 + 32 * (q - BM / 32) + (lane & 31), N - 1);
+        const uint32_t n = (uint32_t)wcol(t, 32 * (q - BM / 32) + (lane & 31), N - 1);
         return (wbase + n) * kRowB + (lane >> 5) * 16;
       };
       vo0 = wave < 4 ? (uint32_t)min(t.m0 + 32 * wave + (lane >> 1), m_last) * kb + half16 : wrow(wave);
       vo1 = wrow(wave + 8);
       if (wave < 4) vo2 = wrow(wave + 16);
-      else if (wave < 6) vo2 = (wbase + (uint32_t)min(t.n0 + 256 * (wave - 4) + 4 * lane, N - 4)) * kScB;
+      else if (wave < 6) vo2 = (wbase + (uint32_t)wcol(t, 256 * (wave - 4) + 4 * lane, N - 4)) * kScB;
       else vo2 = (uint32_t)min(t.m0 + 64 * (wave - 6) + lane, m_last) * ks;
       return;
     }
@@ -493,6 +520,7 @@ void grouped_gemm_kernel(
   // (64 per load, 4 bytes per lane), 2 and 3 the weight rows (256 per load,
   // 16 bytes = 4 rows per lane).
   const uint32_t lds_rs = (uint32_t)(uintptr_t)(lds_void*)&sm.rs[0][0];
+  const uint32_t lds_rw = (uint32_t)(uintptr_t)(lds_void*)&sm.rw[0][0];
   auto issue_rscales = [&](const Tile& t, int rb) __attribute__((always_inline)) {
     const uint32_t dst = lds_rs + (uint32_t)rb * (BM + BN) * 4u;
     if (wave < 2)
@@ -500,8 +528,12 @@ void grouped_gemm_kernel(
                   (uint32_t)min(t.m0 + 64 * wave + lane, t.m0 + t.rows - 1) * 4u, dst + wave * 256u);
     else if (wave < 4)
       lds_dma16_at(reinterpret_cast<const uint8_t*>(w_rscales),
-                   ((uint32_t)t.e * N + min(t.n0 + 256 * (wave - 2) + 4 * lane, N - 4)) * 4u,
+                   ((uint32_t)t.e * N + wcol(t, 256 * (wave - 2) + 4 * lane, N - 4)) * 4u,
                    dst + BM * 4u + (wave - 2) * 1024u);
+    else if (SW && wave < 6 && w_rows)   // the router weights of the tile's rows
+      lds_dma4_at(reinterpret_cast<const uint8_t*>(w_rows),
+                  (uint32_t)min(t.m0 + 64 * (wave - 4) + lane, t.m0 + t.rows - 1) * 4u,
+                  lds_rw + (uint32_t)rb * BM * 4u + (wave - 4) * 256u);
   };
 
   // epilogue: C = (acc * s_A[row]) * s_W[col].  Tile (i, j) of the lane holds
@@ -518,6 +550,77 @@ void grouped_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < FA; ++i) sa[i] = rs_a[32 * i + l32];
     uint8_t* stg = sm.stg[wave];
+    if constexpr (SW) {
+      // h = (silu(g) * u) * w per (row, h column); the 32 x 32 tile of h (and,
+      // if asked for, those of g and u) leave through the staging slice as in
+      // the FP32 path below.
+      const float* rw = sm.rw[rb];
+      float wr[FA];
+#pragma unroll
+      for (int i = 0; i < FA; ++i) wr[i] = w_rows ? rw[32 * i + l32] : 1.0f;
+      float* h_out = static_cast<float*>(c);
+      const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+          h_out + (int64_t)t.m0 * I, (short)0, t.rows * I * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+          gu_out + (int64_t)t.m0 * 2 * I, (short)0, gu_out ? t.rows * 2 * I * 4 : 0, 0x00020000);
+      const int srow = lane >> 3, sch = lane & 7;
+      uint32_t srowI = (uint32_t)(srow * I);
+      asm volatile("" : "+v"(srowI));
+      const int hc = (t.n0 >> 1) + 32 * wave + 4 * sch;        // h column of the lane's stores
+      float4 sg[4], su[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sg[q] = *reinterpret_cast<const float4*>(&rs_w[WN * wave + 8 * q + 4 * h]);
+        su[q] = *reinterpret_cast<const float4*>(&rs_w[WN * wave + 32 + 8 * q + 4 * h]);
+      }
+      auto put = [&](const float4& o, int q) __attribute__((always_inline)) {
+        *reinterpret_cast<float4*>(stg + l32 * 128 + (((2 * q + h) ^ (l32 & 7)) << 4)) = o;
+      };
+      // staged tile -> rows 32 i + (0..31), columns col0 + (0..31) of a matrix with `width` columns
+      auto flush = [&](const __amdgpu_buffer_rsrc_t& rs, int i, uint32_t rowW, uint32_t width, int col)
+          __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 8 * r + srow;
+          const float4 v = *reinterpret_cast<const float4*>(stg + row * 128 + ((sch ^ (row & 7)) << 4));
+          const uint32_t off = ((uint32_t)((32 * i + 8 * r) * width) + rowW + (uint32_t)col) * 4u;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, kNonTemporal);
+        }
+      };
+#pragma unroll
+      for (int i = 0; i < FA; ++i) {
+        float4 g[4], u[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          g[q].x = (acc[i][0][4 * q + 0] * sa[i]) * sg[q].x;
+          g[q].y = (acc[i][0][4 * q + 1] * sa[i]) * sg[q].y;
+          g[q].z = (acc[i][0][4 * q + 2] * sa[i]) * sg[q].z;
+          g[q].w = (acc[i][0][4 * q + 3] * sa[i]) * sg[q].w;
+          u[q].x = (acc[i][1][4 * q + 0] * sa[i]) * su[q].x;
+          u[q].y = (acc[i][1][4 * q + 1] * sa[i]) * su[q].y;
+          u[q].z = (acc[i][1][4 * q + 2] * sa[i]) * su[q].z;
+          u[q].w = (acc[i][1][4 * q + 3] * sa[i]) * su[q].w;
+          float4 hv;
+          hv.x = swiglu_f32(g[q].x, u[q].x, wr[i]);
+          hv.y = swiglu_f32(g[q].y, u[q].y, wr[i]);
+          hv.z = swiglu_f32(g[q].z, u[q].z, wr[i]);
+          hv.w = swiglu_f32(g[q].w, u[q].w, wr[i]);
+          put(hv, q);
+        }
+        flush(rh, i, srowI, (uint32_t)I, hc);
+        if (gu_out) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) put(g[q], q);
+          flush(rg, i, 2 * srowI, (uint32_t)(2 * I), hc);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) put(u[q], q);
+          flush(rg, i, 2 * srowI, (uint32_t)(2 * I), I + hc);
+        }
+        acc[i][0] = floatx16{};
+        acc[i][1] = floatx16{};
+      }
+      return;
+    }
     constexpr int kOutB = OB ? 2 : 4;             // bytes per output element
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         static_cast<uint8_t*>(c) + (int64_t)t.m0 * N * kOutB, (short)0, t.rows * N * kOutB, 0x00020000);
@@ -675,14 +778,67 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uin
   if (grid >= 8) grid &= ~7ll;
   hipStream_t s = static_cast<hipStream_t>(stream);
 #define GG_LAUNCH(KT, OB)                                                                    \
-  g5::grouped_gemm_kernel<KT, OB><<<(unsigned)grid, g5::kThreads, 0, s>>>(                    \
+  g5::grouped_gemm_kernel<KT, OB, false><<<(unsigned)grid, g5::kThreads, 0, s>>>(             \
       a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales, (int)N, \
-      (int)K, c)
+      (int)K, c, nullptr, nullptr, 0)
   const bool kt = w_layout == NVFP4_W_KTILED, ob = c_dtype == NVFP4_OUT_BF16;
   if (kt && !ob) GG_LAUNCH(true, false);
   else if (kt) GG_LAUNCH(true, true);
   else if (!ob) GG_LAUNCH(false, false);
   else GG_LAUNCH(false, true);
 #undef GG_LAUNCH
+  return launch_status();
+}
+
+namespace nvfp4moe {
+// w_rows[r] = topk_w[row_to_tk[r]] for the routed rows (the router weight of
+// each row of the expert-grouped buffer); a map entry outside [0, R_cap) gives 0
+__global__ __launch_bounds__(256) void gather_row_weights_kernel(
+    const float* __restrict__ topk_w, const int32_t* __restrict__ row_to_tk,
+    const int32_t* __restrict__ offsets, int E, int64_t R_cap, float* __restrict__ w_rows) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= min((int64_t)offsets[E], R_cap)) return;
+  const int32_t i = row_to_tk[r];
+  w_rows[r] = (i >= 0 && i < R_cap) ? topk_w[i] : 0.0f;
+}
+}  // namespace nvfp4moe
+
+extern "C" NVFP4MOE_API int nvfp4_grouped_gemm_swiglu(
+    const uint8_t* a_codes, const uint8_t* a_bscales, const float* a_rscales,
+    const int32_t* expert_offsets, int32_t E, int64_t R_cap, const uint8_t* w_codes,
+    const uint8_t* w_bscales, const float* w_rscales, int64_t I, int64_t K, const float* topk_w,
+    const int32_t* row_to_tk, float* h, float* gu, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (E < 1 || E > NVFP4MOE_MAX_EXPERTS || R_cap < 0) return NVFP4_ERR_SHAPE;
+  if (K <= 0 || K % g5::BK != 0 || K > 65536) return NVFP4_ERR_SHAPE;
+  if (I < g5::BN / 2 || I % (g5::BN / 2) != 0 || 2 * I > (1 << 20)) return NVFP4_ERR_SHAPE;
+  if (R_cap > INT32_MAX / 2 || (int64_t)E * 2 * I > INT32_MAX) return NVFP4_ERR_SHAPE;
+  if (R_cap * (K / 2) > (int64_t)UINT32_MAX || (int64_t)E * 2 * I * (K / 2) > (int64_t)UINT32_MAX)
+    return NVFP4_ERR_SHAPE;
+  if (R_cap == 0) return NVFP4_OK;
+  if (!a_codes || !a_bscales || !a_rscales || !expert_offsets || !w_codes || !w_bscales ||
+      !w_rscales || !h)
+    return NVFP4_ERR_NULL;
+  if (topk_w && (!row_to_tk || !workspace)) return NVFP4_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(a_bscales) || !aligned16(a_rscales) ||
+      !aligned16(w_codes) || !aligned16(w_bscales) || !aligned16(w_rscales) || !aligned16(h) ||
+      !aligned16(gu) || !aligned16(workspace))
+    return NVFP4_ERR_ALIGN;
+  if (topk_w && workspace_bytes < (size_t)R_cap * sizeof(float)) return NVFP4_ERR_WORKSPACE;
+  const int64_t n_tiles = I / (g5::BN / 2);
+  const int64_t max_tiles = ((R_cap + g5::BM - 1) / g5::BM + E) * n_tiles;
+  if (max_tiles > INT32_MAX) return NVFP4_ERR_SHAPE;
+  int64_t grid = max_tiles < 256 ? max_tiles : 256;
+  if (grid >= 8) grid &= ~7ll;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* w_rows = nullptr;
+  if (topk_w) {
+    w_rows = static_cast<float*>(workspace);
+    gather_row_weights_kernel<<<(unsigned)((R_cap + 255) / 256), 256, 0, s>>>(
+        topk_w, row_to_tk, expert_offsets, E, R_cap, w_rows);
+  }
+  g5::grouped_gemm_kernel<true, false, true><<<(unsigned)grid, g5::kThreads, 0, s>>>(
+      a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales,
+      (int)(2 * I), (int)K, h, w_rows, gu, (int)I);
   return launch_status();
 }

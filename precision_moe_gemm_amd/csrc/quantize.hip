@@ -733,6 +733,38 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
   store_row<NCH>(o, sw, I, r, codes, bscales, rscales);
 }
 
+// FP32 rows (the weighted SwiGLU output of the fused gate_up GEMM): the row
+// quantiser on rows [0, min(offsets[E], rows)) (all rows when offsets is null);
+// the row amax is taken in registers while the row is read for quantisation.
+template <int NCH>
+__global__ __launch_bounds__(256) void quantize_rows_f32_kernel(
+    const float* __restrict__ x, int64_t rows, int K, const int32_t* __restrict__ offsets, int E,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales, float* __restrict__ rscales) {
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= rows || (offsets && r >= offsets[E])) return;
+  const int lane = lane_id();
+  const float* xrow = x + r * (int64_t)K;
+  float v[NCH][8];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int base = c * kChunk + lane * 8;
+    if (base < K) {
+      const float4 a = *reinterpret_cast<const float4*>(xrow + base);
+      const float4 b = *reinterpret_cast<const float4*>(xrow + base + 4);
+      v[c][0] = a.x; v[c][1] = a.y; v[c][2] = a.z; v[c][3] = a.w;
+      v[c][4] = b.x; v[c][5] = b.y; v[c][6] = b.z; v[c][7] = b.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[c][j] = 0.0f;
+    }
+  }
+  RowCodes<NCH> o;
+  quantize_lane_row<NCH>(v, o);
+  uint32_t sw[(NCH + 7) / 8];
+  pack_scales<NCH>(o, sw);
+  store_row<NCH>(o, sw, K, r, codes, bscales, rscales);
+}
+
 // ------------------------------------------------------------------ dispatch
 inline int nch_for(int64_t K) {
   return K <= 512 ? 1 : K <= 1024 ? 2 : K <= 2048 ? 4 : K <= 4096 ? 8 : 16;
@@ -796,7 +828,6 @@ NVFP4MOE_API size_t nvfp4moe_permute_workspace_size(int64_t T, int32_t k, int32_
 
 NVFP4MOE_API size_t nvfp4moe_workspace_size(int32_t op, int64_t T, int32_t E, int32_t k,
                                             int64_t R_max, int64_t N) {
-  (void)R_max;
   (void)N;
   switch (op) {
     case NVFP4MOE_OP_QUANTIZE_PERMUTE: return nvfp4moe_permute_workspace_size(T, k, E);
@@ -806,6 +837,8 @@ NVFP4MOE_API size_t nvfp4moe_workspace_size(int32_t op, int64_t T, int32_t E, in
     case NVFP4MOE_OP_UNPERMUTE_COMBINE:
     case NVFP4MOE_OP_BF16_GROUPED_GEMM:
     case NVFP4MOE_OP_SWIGLU_BACKWARD: return 0;
+    case NVFP4MOE_OP_GROUPED_GEMM_SWIGLU:
+      return R_max < 0 ? 0 : (((size_t)R_max * sizeof(float) + 255) & ~(size_t)255);
     default: return (size_t)-1;
   }
 }
@@ -827,6 +860,22 @@ NVFP4MOE_API int nvfp4_quantize_rows(const uint16_t* x, int64_t rows, int64_t K,
     quantize_rows_c_kernel<4><<<grid, 256, 0, s>>>(x, rows, (int)K, codes, bscales, rscales);
   else
     NVFP4_DISPATCH_NCH(K, quantize_rows_kernel, grid, s, x, rows, (int)K, codes, bscales, rscales);
+  return launch_status();
+}
+
+NVFP4MOE_API int nvfp4_quantize_rows_f32(const float* x, int64_t rows, int64_t K,
+                                         const int32_t* expert_offsets, int32_t E, uint8_t* codes,
+                                         uint8_t* bscales, float* rscales, void* stream) {
+  if (rows < 0 || K <= 0 || K % 16 != 0 || K > NVFP4MOE_MAX_K) return NVFP4_ERR_SHAPE;
+  if (expert_offsets && (E < 1 || E > NVFP4MOE_MAX_EXPERTS)) return NVFP4_ERR_SHAPE;
+  if (rows == 0) return NVFP4_OK;
+  if (!x || !codes || !bscales || !rscales) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(bscales) || !aligned16(rscales))
+    return NVFP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  NVFP4_DISPATCH_NCH(K, quantize_rows_f32_kernel, grid, s, x, rows, (int)K, expert_offsets, E, codes,
+                     bscales, rscales);
   return launch_status();
 }
 

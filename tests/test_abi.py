@@ -191,3 +191,20 @@ def test_scale_and_code_indices_match_the_layouts():
                 assert pmg.code_index(r, i, K, G) == pos_c[lab_c[r, i // 2]]
     assert pmg.bscale_index(0, 8, 128) == -1 and pmg.code_index(0, 128, 128) == -1
     assert pmg.bscale_index(0, 0, 96, 4) == -1                         # K-tiled needs K % 64
+
+
+def test_fused_swiglu_host_checks(lib):
+    f = lib.nvfp4_grouped_gemm_swiglu
+    #            A                      off   E    R_cap  W                  I    K     topk_w map   h     gu    ws    wsb     stream
+    call = lambda **kw: f(FAKE, FAKE, FAKE, FAKE, 128, 32768, FAKE, FAKE, FAKE, kw.get("I", 768), 2048,
+                          kw.get("tw", FAKE), kw.get("map", FAKE), FAKE, None, kw.get("ws", FAKE),
+                          kw.get("wsb", 32768 * 4), None)
+    assert call(I=640) == ERR_SHAPE                         # I % 256
+    assert call(map=None) == ERR_NULL                       # router weights need the row map
+    assert call(ws=None) == ERR_NULL
+    assert call(wsb=32768 * 4 - 1) == ERR_WORKSPACE
+    assert pmg.workspace_size(pmg.OP_GROUPED_GEMM_SWIGLU, R_max=32768) == 32768 * 4
+    q = lib.nvfp4_quantize_rows_f32
+    assert q(FAKE, 4, 24, None, 0, FAKE, FAKE, FAKE, None) == ERR_SHAPE
+    assert q(FAKE, 4, 32, FAKE, 0, FAKE, FAKE, FAKE, None) == ERR_SHAPE   # offsets with E = 0
+    assert q(FAKE + 4, 4, 32, None, 0, FAKE, FAKE, FAKE, None) == ERR_ALIGN
