@@ -41,6 +41,8 @@ def parse():
     # the GPU clock needs some tens of ms of sustained load to settle: warm up for ~40 ms
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--routing", default="softmax", choices=["softmax", "uniform", "zipf"])
+    p.add_argument("--single-routing", action="store_true",
+                   help="time the headline routing only (skip the other two routings' steps)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-comparisons", action="store_true",
                    help="skip the BF16 forward and NVFP4 input-gradient timings after the timed steps")
@@ -118,7 +120,7 @@ def main():
     dy_bits = W.grad_output_bf16(S, cfg)
     x, dy = bf16(x_bits), bf16(dy_bits)
     ids = torch.from_numpy(ids_np).to(dev)
-    tw = torch.from_numpy(tw_np.reshape(-1)).to(dev)
+    tw = torch.from_numpy(np.ascontiguousarray(tw_np.reshape(-1))).to(dev)
     wgu, wd, wqkv = bf16(wgu_bits), bf16(wd_bits), bf16(wqkv_bits)
     # NVFP4 weights, quantised once (per output row FP32 scale) straight into
     # the K-tiled layout the grouped GEMM reads one contiguous block per K-step
@@ -155,26 +157,37 @@ def main():
     setup_s = time.time() - t0
 
     off = perm["expert_offsets"]
+    r2t = perm["row_to_tk"]
+    hbuf = torch.empty(R, I, dtype=torch.float32, device=dev)
+    fws = torch.empty(pmg.workspace_size(pmg.OP_GROUPED_GEMM_SWIGLU, R_max=R), dtype=torch.uint8, device=dev)
+    a_perm = (perm["codes"], perm["bscales"], perm["rscales"], off)
+    mid_plain = [
+        ("gate_up_gemm", lambda: pmg.nvfp4_grouped_gemm(*a_perm, *q_gu, c=gu)),
+        ("swiglu_quantize", lambda: pmg.swiglu_quantize(gu, off, tw, r2t, out=a2)),
+    ]
+    # the weighted SwiGLU (FP32) in the gate_up GEMM's epilogue; gate/up kept for the backward
+    mid_fused = [
+        ("gate_up_gemm_swiglu", lambda: pmg.nvfp4_grouped_gemm_swiglu(*a_perm, *q_gu, topk_w=tw, row_to_tk=r2t,
+                                                                      h=hbuf, gu=gu, workspace=fws)),
+        ("quantize_h", lambda: pmg.nvfp4_quantize_rows_f32(hbuf, off, a2["codes"], a2["bscales"], a2["rscales"])),
+    ]
     ops = [
         ("qkv_quantize", lambda: pmg.nvfp4_quantize_rows(x, a_qkv["c"], a_qkv["b"], a_qkv["s"])),
         ("qkv_gemm", lambda: pmg.nvfp4_grouped_gemm(a_qkv["c"], a_qkv["b"], a_qkv["s"], qkv_off, *q_qkv, c=qkv)),
         ("quantize_permute", lambda: pmg.nvfp4_quantize_permute(x, ids, E, workspace=ws, out=perm)),
-        ("gate_up_gemm", lambda: pmg.nvfp4_grouped_gemm(perm["codes"], perm["bscales"], perm["rscales"], off,
-                                                        *q_gu, c=gu)),
-        ("swiglu_quantize", lambda: pmg.swiglu_quantize(gu, off, tw, perm["row_to_tk"], out=a2)),
+        *mid_plain,
         ("down_gemm", lambda: pmg.nvfp4_grouped_gemm(a2["codes"], a2["bscales"], a2["rscales"], off, *q_d, c=dn)),
         ("combine", lambda: pmg.unpermute_combine(dn, perm["tk_to_row"], k, y=y)),
         # the output gradient's rows are gathered into expert order inside the GEMM's loads
-        ("dgrad_down_gemm", lambda: pmg.bf16_grouped_gemm_gather(dy, perm["row_to_tk"], k, off, wd, pmg.W_KN,
-                                                                 c=dh)),
-        ("swiglu_backward", lambda: pmg.swiglu_backward(gu, dh, off, tw, perm["row_to_tk"], dgu=dgu)),
+        ("dgrad_down_gemm", lambda: pmg.bf16_grouped_gemm_gather(dy, r2t, k, off, wd, pmg.W_KN, c=dh)),
+        ("swiglu_backward", lambda: pmg.swiglu_backward(gu, dh, off, tw, r2t, dgu=dgu)),
         ("dgrad_gate_up_gemm", lambda: pmg.bf16_grouped_gemm(dgu, off, wgu, pmg.W_KN, c=dx_perm)),
         ("dgrad_combine", lambda: pmg.unpermute_combine(dx_perm, perm["tk_to_row"], k, y=dx)),
     ]
-    n_ops = len(ops)
+    ops_fused = ops[:3] + mid_fused + ops[5:]
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
+    def step(events=None, ops=ops):
         for i, (_, fn) in enumerate(ops):
             if events is not None:
                 events[i][0].record(stream)
@@ -182,34 +195,43 @@ def main():
             if events is not None:
                 events[i][1].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def set_routing(kind):
+        ids_np_, tw_np_ = (ids_np, tw_np) if kind == args.routing else W.make_routing(kind, T, E, k, cfg)
+        ids.copy_(torch.from_numpy(ids_np_))
+        tw.copy_(torch.from_numpy(tw_np_.reshape(-1)))
+        torch.cuda.synchronize()
 
-    # timed region: K full steps, per-op HIP events on the launch stream
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in range(n_ops)] for _ in range(args.steps)]
+    def timed_steps(warmup, ops_=ops):
+        """warmup untimed steps, then --steps timed ones with per-op HIP events on the
+        launch stream; returns (ms per step, {op: ms})"""
+        for _ in range(warmup):
+            step(None, ops_)
+        evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                for _ in range(len(ops_))] for _ in range(args.steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for s_ in range(args.steps):
+            step(evs[s_], ops_)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        op_ms_ = {name: float(np.mean([evs[s_][i][0].elapsed_time(evs[s_][i][1]) for s_ in range(args.steps)]))
+                  for i, (name, _) in enumerate(ops_)}
+        return start.elapsed_time(stop) / args.steps, op_ms_
+
+    # timed region: K full steps of the headline routing
+    ms_step, op_ms = timed_steps(args.warmup)
+    # the same steps with no per-op events, as the baseline of the graph replay
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for s in range(args.steps):
-        step(evs[s])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
-    # the same steps with no per-op events, as the baseline of the graph replay
-    torch.cuda.synchronize()
-    start.record(stream)
-    for s in range(args.steps):
+    for s_ in range(args.steps):
         step()
     stop.record(stream)
     torch.cuda.synchronize()
     ms_step_plain = start.elapsed_time(stop) / args.steps
     graph = graph_steps(step, args.steps, args.warmup, T)
     graph["eager_ms_per_step_no_events"] = round(ms_step_plain, 4)
-    op_ms = {name: float(np.mean([evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(args.steps)]))
-             for i, (name, _) in enumerate(ops)}
 
     # ---------------- algorithmic work per op (useful rows only)
     Rr = int(off[-1].item())
@@ -224,6 +246,7 @@ def main():
     op_bytes = {
         "qkv_quantize": T * H * 2 + T * nvfp4_row(H),
         "quantize_permute": T * H * 2 + T * k * 4 + Rr * nvfp4_row(H) + 2 * Rr * 4 + (E + 1) * 4,
+        "quantize_h": Rr * I * 4 + Rr * nvfp4_row(I),
         "swiglu_quantize": Rr * 2 * I * 4 + Rr * 4 * 2 + Rr * nvfp4_row(I),
         "combine": Rr * H * 4 + T * k * 4 + T * H * 2,
         "swiglu_backward": Rr * 2 * I * 4 + Rr * I * 4 + Rr * 8 + Rr * 2 * I * 2,
@@ -236,27 +259,32 @@ def main():
     op_ms_in_step = dict(op_ms)
     op_ms["quantize_permute"] = qp_cold_us * 1e-3
 
-    per_op = {}
-    for name in op_ms:
-        us = op_ms[name] * 1e3
-        d = {"us": round(us, 2)}
-        if name in gemm_flops:
-            tf = gemm_flops[name] / (us * 1e-6) / 1e12
-            d.update(TFLOPs=round(tf, 1), frac_f16_mfma_peak=round(tf / PEAK_F16_TFLOPS, 4))
-        if name in op_bytes:
-            gbs = op_bytes[name] / (us * 1e-6) / 1e9
-            d.update(GBps=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBPS, 4))
-        per_op[name] = d
+    def per_op_of(op_ms_):
+        out = {}
+        for name in op_ms_:
+            us = op_ms_[name] * 1e3
+            d = {"us": round(us, 2)}
+            if name in gemm_flops:
+                tf = gemm_flops[name] / (us * 1e-6) / 1e12
+                d.update(TFLOPs=round(tf, 1), frac_f16_mfma_peak=round(tf / PEAK_F16_TFLOPS, 4))
+            if name in op_bytes:
+                gbs = op_bytes[name] / (us * 1e-6) / 1e9
+                d.update(GBps=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBPS, 4))
+            out[name] = d
+        return out
+
+    per_op = per_op_of(op_ms)
     per_op["quantize_permute"]["in_step_us"] = round(op_ms_in_step["quantize_permute"] * 1e3, 2)
     per_op["quantize_permute"]["how"] = ("mean over --steps launches, each after a 512 MiB cache-evicting "
                                          "write outside its events; in_step_us: inside the timed step")
 
-    w4_us = (op_ms["gate_up_gemm"] + op_ms["down_gemm"]) * 1e3
-    value = (gemm_flops["gate_up_gemm"] + gemm_flops["down_gemm"]) / (w4_us * 1e-6) / 1e12
+    w4 = lambda om: (gemm_flops["gate_up_gemm"] + gemm_flops["down_gemm"]) / (
+        (om["gate_up_gemm"] + om["down_gemm"]) * 1e-3) / 1e12
+    value = w4(op_ms)
     gu_us = op_ms["gate_up_gemm"] * 1e3
     gu_tf = gemm_flops["gate_up_gemm"] / (gu_us * 1e-6) / 1e12
-    roofline = {"kernel": "nvfp4 grouped GEMM gate_up (grouped_gemm_kernel)", "bound": "mfma",
-                "achieved": round(gu_tf, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+    roofline = {"kernel": "nvfp4 grouped GEMM gate_up (grouped_gemm_kernel<K-tiled, FP32 out>)",
+                "bound": "mfma", "achieved": round(gu_tf, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gu_tf / PEAK_F16_TFLOPS, 4), "traffic": measured_traffic(),
                 "work_per_launch": f"{gemm_flops['gate_up_gemm']:.4e} FLOP (2 * {Rr} rows * 2048 * 1536)",
                 "avg_launch_us": round(gu_us, 2)}
@@ -280,14 +308,39 @@ def main():
         "setup_s": round(setup_s, 1),
     }
 
-    result["gate_up_by_routing"] = gate_up_by_routing(
-        args.routing, gu_us, dict(x=x, E=E, k=k, I=I, H=H, T=T, q_gu=q_gu, gu=gu, ws=ws, cfg=cfg), args.steps)
+    # the other routings of the gate_up workload (uniform k-subsets, Zipf(1.2)):
+    # the same step, timed the same way, after the headline's
+    by_routing = {args.routing: {"ms_per_step": round(ms_step, 4), "value": round(value, 2),
+                                 "gate_up_gemm": per_op["gate_up_gemm"], "down_gemm": per_op["down_gemm"]}}
+    for kind in ("softmax", "uniform", "zipf"):
+        if kind == args.routing or args.single_routing:
+            continue
+        set_routing(kind)
+        ms_k, om_k = timed_steps(min(args.warmup, 5))
+        po = per_op_of(om_k)
+        by_routing[kind] = {"ms_per_step": round(ms_k, 4), "value": round(w4(om_k), 2),
+                            "gate_up_gemm": po["gate_up_gemm"], "down_gemm": po["down_gemm"]}
+    by_routing["how"] = "each routing: warm-up steps, then --steps timed steps with per-op HIP events"
+    result["by_routing"] = by_routing
+    set_routing(args.routing)
+    # the same step with the weighted SwiGLU in the gate_up GEMM's epilogue (FP32)
+    # and the light FP32-row quantiser in place of the float64 SwiGLU-quantise pass
+    ms_f, om_f = timed_steps(min(args.warmup, 5), ops_fused)
+    result["fused_swiglu_step"] = {
+        "ms_per_step": round(ms_f, 4), "layer_tokens_per_s": round(T / (ms_f * 1e-3), 1),
+        "gate_up_gemm_swiglu_us": round(om_f["gate_up_gemm_swiglu"] * 1e3, 2),
+        "quantize_h_us": round(om_f["quantize_h"] * 1e3, 2),
+        "plain_gate_up_gemm_plus_swiglu_quantize_us": round((op_ms["gate_up_gemm"] + op_ms["swiglu_quantize"]) * 1e3, 2),
+        "how": "warm-up steps, then --steps timed steps, after the headline routing's; same buffers"}
+    step()
+    torch.cuda.synchronize()
+
     result["practical_ceiling"] = practical_ceiling(gu_tf, per_op["quantize_permute"]["GBps"])
     if not args.no_comparisons:
         result["comparisons"] = comparisons(
-            dict(x=x, dy=dy, ids=ids, E=E, k=k, I=I, H=H, perm=perm, wgu=wgu, wd=wd, dgu=dgu, ws=ws,
-                 q_gu=q_gu, tw=tw, gu=gu, a2=a2),
-            gemm_flops, op_ms)
+            dict(x=x, dy=dy, ids=ids, E=E, k=k, I=I, H=H, perm=perm, wgu=wgu, wd=wd, dgu=dgu, dh=dh, ws=ws,
+                 q_gu=q_gu, q_d=q_d, tw=tw, gu=gu, a2=a2, hbuf=hbuf, fws=fws, dn=dn, dx_perm=dx_perm),
+            gemm_flops)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_bits, ids_np, wgu_bits, S, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -315,30 +368,6 @@ def time_cold(fn, reps):
         en.record(stream)
     torch.cuda.synchronize()
     return float(np.mean([st.elapsed_time(en) for st, en in evs])) * 1e3
-
-
-def gate_up_by_routing(step_routing, step_us, t, reps):
-    """The gate_up GEMM under the three routings of the same tokens (softmax
-    top-8, uniform 8-subsets, Zipf(1.2)), each timed over `reps` launches after
-    the timed steps, on the step's weights and output buffer."""
-    import torch
-    import precision_moe_gemm_amd as pmg
-    import workloads as W
-    T, E, k, I, H, x = t["T"], t["E"], t["k"], t["I"], t["H"], t["x"]
-    out = {f"{step_routing}_in_step": {"us": round(step_us, 2)}}
-    for kind in ("softmax", "uniform", "zipf"):
-        ids_np, _ = W.make_routing(kind, T, E, k, t["cfg"])
-        perm = pmg.nvfp4_quantize_permute(x, torch.from_numpy(ids_np).to(x.device), E, workspace=t["ws"])
-        off = perm["expert_offsets"]
-        out[kind] = {"us": round(_time_op(lambda: pmg.nvfp4_grouped_gemm(
-            perm["codes"], perm["bscales"], perm["rscales"], off, *t["q_gu"], c=t["gu"]), reps), 2)}
-        del perm
-    for kind, d in out.items():
-        tf = 2.0 * T * k * H * 2 * I / (d["us"] * 1e-6) / 1e12
-        d.update(TFLOPs=round(tf, 1), frac_f16_mfma_peak=round(tf / PEAK_F16_TFLOPS, 4))
-    out["how"] = (f"{step_routing}_in_step: the timed steps' figure; per routing: 3 untimed + {reps} timed "
-                  "back-to-back launches after the steps, same weights and output buffer")
-    return out
 
 
 def cpu_model():
@@ -396,35 +425,55 @@ def _time_op(fn, reps=10):
     return st.elapsed_time(en) * 1e3 / reps
 
 
-def comparisons(t, gemm_flops, op_ms):
-    """The same layer at other precisions, timed after the timed steps (outside them):
-    the forward's expert GEMMs in BF16 (the precision NVFP4 replaces), and the
-    input gradient's GEMMs in NVFP4 (a lower-precision backward: the output
-    gradient quantised and permuted like the forward input, the SwiGLU gradient
-    quantised per row, the forward weights transposed and quantised along their
-    output dimension once, untimed)."""
+def comparisons(t, gemm_flops):
+    """The layer's GEMMs at other precisions and the SwiGLU unfused, timed after the
+    timed steps (outside them).  Both sides of every comparison are timed the same
+    way (3 untimed + 10 timed back-to-back launches, HIP events on the launch
+    stream): back-to-back GEMMs hold the matrix cores busy long enough to lower
+    the clock, so these figures run slower than the same kernels inside a step and
+    are compared only with each other.
+      bf16_forward: the forward's expert GEMMs in BF16 (the precision NVFP4
+        replaces) against the step's NVFP4 ones;
+      nvfp4_input_gradient: the input gradient's GEMMs in NVFP4 (a lower-precision
+        backward: the output gradient quantised and permuted like the forward
+        input, the SwiGLU gradient quantised per row, the forward weights
+        transposed and quantised along their output dimension once, untimed)
+        against the step's BF16 ones;
+      fused_swiglu_gate_up: the step's gate_up with the FP32 SwiGLU in its
+        epilogue + the FP32-row quantiser, against the plain gate_up GEMM + the
+        float64 SwiGLU-quantise pass."""
     import torch
     import precision_moe_gemm_amd as pmg
     x, dy, ids, E, k, I, H = t["x"], t["dy"], t["ids"], t["E"], t["k"], t["I"], t["H"]
     perm, off = t["perm"], t["perm"]["expert_offsets"]
-    R = perm["row_to_tk"].numel()
+    r2t = perm["row_to_tk"]
+    a = (perm["codes"], perm["bscales"], perm["rscales"], off)
+    a2 = t["a2"]
+    R = r2t.numel()
     dev = x.device
     tf = lambda name, us: round(gemm_flops[name] / (us * 1e-6) / 1e12, 1)
     out = {}
+    # the step's NVFP4 forward GEMMs, timed as the comparisons are
+    us_nv_gu = _time_op(lambda: pmg.nvfp4_grouped_gemm(*a, *t["q_gu"], c=t["gu"]))
+    us_nv_dn = _time_op(lambda: pmg.nvfp4_grouped_gemm(a2["codes"], a2["bscales"], a2["rscales"], off, *t["q_d"],
+                                                       c=t["dn"]))
     # BF16 forward: gate_up reads the token rows through the routing map, down a BF16 SwiGLU output
     gu_bf = torch.empty(R, 2 * I, dtype=torch.float32, device=dev)
     h16 = t["dgu"][:, :I].contiguous()
     dn_bf = torch.empty(R, H, dtype=torch.float32, device=dev)
-    us_gu = _time_op(lambda: pmg.bf16_grouped_gemm_gather(x, perm["row_to_tk"], k, off, t["wgu"], pmg.W_NK,
-                                                          c=gu_bf))
+    us_gu = _time_op(lambda: pmg.bf16_grouped_gemm_gather(x, r2t, k, off, t["wgu"], pmg.W_NK, c=gu_bf))
     us_dn = _time_op(lambda: pmg.bf16_grouped_gemm(h16, off, t["wd"], pmg.W_NK, c=dn_bf))
-    nv = (op_ms["gate_up_gemm"] + op_ms["down_gemm"]) * 1e3
     out["bf16_forward"] = {
         "gate_up_gemm": {"us": round(us_gu, 2), "TFLOPs": tf("gate_up_gemm", us_gu)},
         "down_gemm": {"us": round(us_dn, 2), "TFLOPs": tf("down_gemm", us_dn)},
-        "nvfp4_gemms_speedup": round((us_gu + us_dn) / nv, 3)}
+        "nvfp4_gate_up_gemm": {"us": round(us_nv_gu, 2), "TFLOPs": tf("gate_up_gemm", us_nv_gu)},
+        "nvfp4_down_gemm": {"us": round(us_nv_dn, 2), "TFLOPs": tf("down_gemm", us_nv_dn)},
+        "nvfp4_gemms_speedup": round((us_gu + us_dn) / (us_nv_gu + us_nv_dn), 3)}
     del gu_bf, dn_bf, h16
-    # NVFP4 input gradient
+    # NVFP4 input gradient against the step's BF16 dgrad GEMMs
+    us_bf_dd = _time_op(lambda: pmg.bf16_grouped_gemm_gather(dy, r2t, k, off, t["wd"], pmg.W_KN, c=t["dh"]))
+    us_bf_dg = _time_op(lambda: pmg.bf16_grouped_gemm(t["dgu"], off, t["wgu"], pmg.W_KN, c=t["dx_perm"]))
+
     def transposed_nvfp4(w):     # [E, out, in] -> quantised [E, in, out] along out, K-tiled
         wt = pmg.bf16_transpose(w)
         c_, b_, s_ = pmg.nvfp4_quantize_rows_tiled(wt.view(-1, wt.shape[2]), wt.shape[1])
@@ -446,7 +495,7 @@ def comparisons(t, gemm_flops, op_ms):
                                                     pdy["expert_offsets"], *q_dt, c=dh))
     us_q = _time_op(lambda: pmg.nvfp4_quantize_rows(t["dgu"], *g))
     us_dg = _time_op(lambda: pmg.nvfp4_grouped_gemm(*g, pdy["expert_offsets"], *q_gut, c=dxp))
-    bf = (op_ms["dgrad_down_gemm"] + op_ms["dgrad_gate_up_gemm"]) * 1e3
+    bf = us_bf_dd + us_bf_dg
     total = us_qp + us_dd + us_q + us_dg
     out["nvfp4_input_gradient"] = {
         "grad_quantize_permute": {"us": round(us_qp, 2)},
@@ -455,27 +504,23 @@ def comparisons(t, gemm_flops, op_ms):
         "dgrad_gate_up_gemm": {"us": round(us_dg, 2), "TFLOPs": tf("dgrad_gate_up_gemm", us_dg)},
         "total_us": round(total, 2), "bf16_dgrad_gemms_us": round(bf, 2),
         "speedup_vs_bf16": round(bf / total, 3)}
-    # the weighted SwiGLU fused into the gate_up GEMM's epilogue (FP32 SwiGLU), then the
-    # FP32-row quantiser, against gate_up GEMM + the float64 SwiGLU-quantise pass; once
-    # without the gate/up output (forward only) and once with it (kept for the backward)
-    h = torch.empty(R, I, dtype=torch.float32, device=dev)
-    fws = torch.empty(pmg.workspace_size(pmg.OP_GROUPED_GEMM_SWIGLU, R_max=R), dtype=torch.uint8, device=dev)
-    a = (perm["codes"], perm["bscales"], perm["rscales"], off)
-    a2 = t["a2"]
-    fused = lambda gu_out: pmg.nvfp4_grouped_gemm_swiglu(*a, *t["q_gu"], topk_w=t["tw"], row_to_tk=perm["row_to_tk"],
-                                                         h=h, gu=gu_out, workspace=fws)
+    del pdy, g, dh, dxp, q_dt, q_gut
+    # fused SwiGLU: without the gate/up output (forward only) and with it (kept for the backward)
+    fused = lambda gu_out: pmg.nvfp4_grouped_gemm_swiglu(*a, *t["q_gu"], topk_w=t["tw"], row_to_tk=r2t,
+                                                         h=t["hbuf"], gu=gu_out, workspace=t["fws"])
     us_f = _time_op(lambda: fused(None))
     us_fg = _time_op(lambda: fused(t["gu"]))
-    us_q = _time_op(lambda: pmg.nvfp4_quantize_rows_f32(h, off, a2["codes"], a2["bscales"], a2["rscales"]))
-    sep = (op_ms["gate_up_gemm"] + op_ms["swiglu_quantize"]) * 1e3
+    us_qh = _time_op(lambda: pmg.nvfp4_quantize_rows_f32(t["hbuf"], off, a2["codes"], a2["bscales"], a2["rscales"]))
+    us_sq = _time_op(lambda: pmg.swiglu_quantize(t["gu"], off, t["tw"], r2t, out=a2))
+    sep = us_nv_gu + us_sq
     out["fused_swiglu_gate_up"] = {
         "gemm_swiglu_us": round(us_f, 2), "gemm_swiglu_with_gu_us": round(us_fg, 2),
-        "quantize_h_us": round(us_q, 2),
-        "separate_gemm_plus_swiglu_quantize_us": round(sep, 2),
-        "speedup_forward_only": round(sep / (us_f + us_q), 3),
-        "speedup_with_gu": round(sep / (us_fg + us_q), 3)}
-    out["how"] = ("after the timed steps: 3 untimed + 10 timed launches per op, HIP events on the "
-                  "launch stream; same routing, shapes and buffers as the step")
+        "quantize_h_us": round(us_qh, 2), "plain_gate_up_gemm_us": round(us_nv_gu, 2),
+        "swiglu_quantize_f64_us": round(us_sq, 2),
+        "speedup_forward_only": round(sep / (us_f + us_qh), 3),
+        "speedup_with_gu": round(sep / (us_fg + us_qh), 3)}
+    out["how"] = ("after the timed steps: 3 untimed + 10 timed back-to-back launches per op, HIP events on "
+                  "the launch stream, both sides of each comparison alike; same routing, shapes and buffers")
     return out
 
 

@@ -250,9 +250,9 @@ NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_bsc
  * expert e and h column j in [0, I):
  *     g = C[r][j], u = C[r][I + j]  (C = A W_e^T as nvfp4_grouped_gemm computes it, FP32)
  *     h[r][j] = (silu(g) * u) * w_r,  silu(g) = g / (1 + exp(-g)),  in FP32
- * with w_r = topk_w[row_to_tk[r]] (1 when topk_w is NULL).  exp is the hardware
- * exp2 of -g log2(e): h lies within 2^-20 |h64| + 2^-24 max_row |h64| of the
- * float64 value h64 of the same g and u.  Quantise h with nvfp4_quantize_rows_f32
+ * with w_r = topk_w[row_to_tk[r]] (1 when topk_w is NULL).  exp and the
+ * division are the hardware exp2 of -g log2(e) and reciprocal: h lies within
+ * 2^-20 |h64| + 2^-24 max_row |h64| of the float64 value h64 of the same g and u.  Quantise h with nvfp4_quantize_rows_f32
  * (its amax is taken while it reads h).
  *   A, expert_offsets, E, R_cap, K: as nvfp4_grouped_gemm
  *   W: K-tiled only, w_codes [E][K/64][2I][32], w_bscales [E][K/64][2I][4],

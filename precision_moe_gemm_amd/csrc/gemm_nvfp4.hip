@@ -207,13 +207,14 @@ __device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_star
 }
 
 // Weighted SwiGLU of one gate/up pair in FP32: h = (silu(g) * u) * w, with
-// silu(g) = g / (1 + exp(-g)) (hardware exp2 of -g log2(e), correctly rounded
-// division).  Within a few FP32 ulps of the float64 value wherever |h| is not
-// negligible next to the row's largest |h| (for g far below zero exp(-g)
-// carries a relative error of about |g| 2^-24, while silu(g) is tiny).
+// silu(g) = g / (1 + exp(-g)) formed as g * rcp(1 + exp2(-g log2(e))) from the
+// hardware exp2 and reciprocal (about 1 ulp each).  Within a few FP32 ulps of
+// the float64 value wherever |h| is not negligible next to the row's largest
+// |h| (for g far below zero exp(-g) carries a relative error of about
+// |g| 2^-24, while silu(g) is tiny); 1 + exp(-g) = inf gives silu = -0.
 __device__ __forceinline__ float swiglu_f32(float g, float u, float w) {
-  const float e = __expf(-g);
-  return ((g / (1.0f + e)) * u) * w;
+  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return ((g * __builtin_amdgcn_rcpf(1.0f + e)) * u) * w;
 }
 
 // KT: K-tiled weights; OB: BF16 output (each FP32 result rounded to nearest

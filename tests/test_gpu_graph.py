@@ -16,7 +16,7 @@ from helpers import bf16_dev, dev, gpu_ready
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_ready(), reason="needs a GPU")]
 
-T, H, E, K_TOP, I = 256, 256, 8, 4, 128
+T, H, E, K_TOP, I = 256, 256, 8, 4, 256
 
 
 def _tiled(w2d, n):
@@ -43,6 +43,9 @@ def test_layer_step_graph_replays_match_eager():
     gu, dn, dh, dxp = emp((R, 2 * I), f32), emp((R, H), f32), emp((R, I), f32), emp((R, H), f32)
     a2 = {"codes": emp((R, I // 2), u8), "bscales": emp((R, I // 16), u8), "rscales": emp((R,), f32)}
     y, dx, dgu = emp((T, H), b16), emp((T, H), b16), emp((R, 2 * I), b16)
+    h, gu2 = emp((R, I), f32), emp((R, 2 * I), f32)
+    a3 = {"codes": emp((R, I // 2), u8), "bscales": emp((R, I // 16), u8), "rscales": emp((R,), f32)}
+    fws = emp((pmg.workspace_size(pmg.OP_GROUPED_GEMM_SWIGLU, R_max=R),), u8)
     off = perm["expert_offsets"]
 
     def step():
@@ -55,8 +58,13 @@ def test_layer_step_graph_replays_match_eager():
         pmg.swiglu_backward(gu, dh, off, tw, perm["row_to_tk"], dgu=dgu)
         pmg.bf16_grouped_gemm(dgu, off, wgu, pmg.W_KN, c=dxp)
         pmg.unpermute_combine(dxp, perm["tk_to_row"], K_TOP, y=dx)
+        # the fused gate_up + SwiGLU path (router-weight gather + GEMM) and its quantiser
+        pmg.nvfp4_grouped_gemm_swiglu(perm["codes"], perm["bscales"], perm["rscales"], off, *q_gu, topk_w=tw,
+                                      row_to_tk=perm["row_to_tk"], h=h, gu=gu2, workspace=fws)
+        pmg.nvfp4_quantize_rows_f32(h, off, a3["codes"], a3["bscales"], a3["rscales"])
 
-    outs = {"y": y, "dx": dx, "gu": gu, "dn": dn, "dh": dh, "dgu": dgu, "dxp": dxp,
+    outs = {"y": y, "dx": dx, "gu": gu, "dn": dn, "dh": dh, "dgu": dgu, "dxp": dxp, "h": h, "gu2": gu2,
+            **{f"a3.{k}": v for k, v in a3.items()},
             **{f"perm.{k}": v for k, v in perm.items()}, **{f"a2.{k}": v for k, v in a2.items()}}
     step()
     torch.cuda.synchronize()
