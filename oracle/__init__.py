@@ -33,5 +33,6 @@ Modules:
   swiglu    - weighted SwiGLU + NVFP4 quantisation, and its backward
   combine   - un-permutation with top-k combine, and the gather for dgrad
   layer     - the chained MoE layer forward and BF16 dgrad backward
+  wgrad     - the expert weight gradient in NVFP4, quantised along tokens
 """
-from . import formats, quantize, permute, gemm, swiglu, combine, layer  # noqa: F401
+from . import formats, quantize, permute, gemm, swiglu, combine, layer, wgrad  # noqa: F401
