@@ -519,9 +519,72 @@ def comparisons(t, gemm_flops):
         "swiglu_quantize_f64_us": round(us_sq, 2),
         "speedup_forward_only": round(sep / (us_f + us_qh), 3),
         "speedup_with_gu": round(sep / (us_fg + us_qh), 3)}
+    out["nvfp4_weight_gradient"] = weight_gradients(t)
     out["how"] = ("after the timed steps: 3 untimed + 10 timed back-to-back launches per op, HIP events on "
                   "the launch stream, both sides of each comparison alike; same routing, shapes and buffers")
     return out
+
+
+def weight_gradients(t):
+    """The expert weight gradients dW_d[e] = dY_e^T h_e and dW_gu[e] = dGU_e^T x_e in
+    NVFP4, quantised along tokens (each operand's per-expert slab, one FP32 scale per
+    (expert, channel), E4M3 per 16 tokens; one K-grouped GEMM launch over all
+    experts), against BF16 torch.bmm (hipBLASLt) on the same products with every
+    expert's tokens zero-padded to the largest expert's count (padding done
+    before timing)."""
+    import torch
+    import precision_moe_gemm_amd as pmg
+    x, dy, E, k, I, H = t["x"], t["dy"], t["E"], t["k"], t["I"], t["H"]
+    perm = t["perm"]
+    off, r2t = perm["expert_offsets"], perm["row_to_tk"]
+    R = r2t.numel()
+    kofs = pmg.token_blocks(off)
+    Kp = pmg.token_capacity(R, E)
+    off_h = off.cpu().numpy()
+    r2t_l = r2t.long()
+    n_max = int(np.diff(off_h).max())
+    flops = 2.0 * R * H * I
+    res = {}
+
+    def padded(rows):           # [R][C] expert-grouped -> [E][n_max][C], zero rows past each expert
+        outp = torch.zeros(E, n_max, rows.shape[1], dtype=torch.bfloat16, device=rows.device)
+        for e in range(E):
+            o0, o1 = int(off_h[e]), int(off_h[e + 1])
+            outp[e, : o1 - o0] = rows[o0:o1].to(torch.bfloat16)
+        return outp
+
+    for name, g, g_map, xx, x_map, M, N in (
+            ("down", dy, True, t["hbuf"], False, H, I),
+            ("gate_up", t["dgu"], False, x, True, 2 * I, H)):
+        gq = pmg.nvfp4_quantize_tokens(g, off, kofs, Kp, pmg.W_ROWMAJOR, row_to_tk=r2t if g_map else None, k=k)
+        xq = pmg.nvfp4_quantize_tokens(xx, off, kofs, Kp, pmg.W_KTILED, row_to_tk=r2t if x_map else None, k=k)
+        dw = torch.empty(E, M, N, dtype=torch.float32, device=x.device)
+        dw16 = torch.empty(E, M, N, dtype=torch.bfloat16, device=x.device)
+        us_g = _time_op(lambda: pmg.nvfp4_quantize_tokens(g, off, kofs, Kp, pmg.W_ROWMAJOR,
+                                                          row_to_tk=r2t if g_map else None, k=k,
+                                                          out=dict(zip(("codes", "bscales", "rscales"), gq))))
+        us_x = _time_op(lambda: pmg.nvfp4_quantize_tokens(xx, off, kofs, Kp, pmg.W_KTILED,
+                                                          row_to_tk=r2t if x_map else None, k=k,
+                                                          out=dict(zip(("codes", "bscales", "rscales"), xq))))
+        us_mm = _time_op(lambda: pmg.nvfp4_grouped_gemm_wgrad(gq, xq, kofs, c=dw))
+        us_mm16 = _time_op(lambda: pmg.nvfp4_grouped_gemm_wgrad(gq, xq, kofs, c=dw16))
+        del dw, dw16, gq, xq
+        g_rows = g[r2t_l // k] if g_map else g
+        x_rows = xx[r2t_l // k] if x_map else xx
+        gp = padded(g_rows).transpose(1, 2).contiguous()          # [E][M][n_max]
+        xp = padded(x_rows)                                        # [E][n_max][N]
+        del g_rows, x_rows
+        dwb = torch.empty(E, M, N, dtype=torch.bfloat16, device=x.device)
+        us_bf = _time_op(lambda: torch.bmm(gp, xp, out=dwb))
+        del gp, xp, dwb
+        total = us_g + us_x + us_mm16
+        res[name] = {"quantize_grad_us": round(us_g, 2), "quantize_input_us": round(us_x, 2),
+                     "gemm_f32_out_us": round(us_mm, 2), "gemm_bf16_out_us": round(us_mm16, 2),
+                     "gemm_bf16_out_TFLOPs": round(flops / (us_mm16 * 1e-6) / 1e12, 1),
+                     "total_bf16_out_us": round(total, 2), "bf16_bmm_padded_us": round(us_bf, 2),
+                     "speedup_vs_bf16": round(us_bf / total, 3)}
+    res["padded_tokens_per_expert"] = n_max
+    return res
 
 
 def practical_ceiling(gate_up_tflops, qp_gbps):

@@ -284,6 +284,64 @@ NVFP4MOE_API int nvfp4_quantize_rows_f32(const float* x, int64_t rows, int64_t K
                                          uint8_t* bscales, float* rscales, void* stream);
 
 /*
+ * The expert weight gradient in NVFP4, quantised along tokens (the blog "miniTE
+ * NVFP4", section "Two complementary interventions": the backward's precision
+ * is chosen independently of the forward's; a lower-bit backward is not
+ * automatically faster).  For expert e with rows [offsets[e], offsets[e+1]):
+ *     dW_e[m][n] = sum over its rows r of  G[r][m] * X[r][n]
+ * (G the output gradient of the expert GEMM, X its input).  Both operands are
+ * quantised along the contraction, i.e. along the expert's tokens: the slab
+ * X_e^T [C][K_e] (K_e = the expert's rows rounded up to a multiple of 64, at
+ * least 64, extra tokens zero) is quantised row by row with the definition at
+ * the top of this header (one FP32 scale per (expert, channel), one E4M3 scale
+ * per 16 tokens).  The slabs of all experts sit side by side along K: expert
+ * e's tokens are K positions [64 kofs[e], 64 kofs[e+1]).
+ *
+ * nvfp4moe_token_blocks - kofs[E+1] (device int32) from expert_offsets: each
+ * expert takes max(1, ceil(rows / 64)) steps of 64 tokens; kofs[E] <= R/64 + E.
+ *
+ * nvfp4_quantize_tokens - the slabs of all experts.
+ *   x        [x_rows][C] of x_dtype (NVFP4_IN_BF16 bits or NVFP4_IN_F32)
+ *   row_to_tk, k: if given, row r of the expert-grouped order is x row
+ *            row_to_tk[r] / k (token order input, e.g. the output gradient);
+ *            NULL: x is already in the expert-grouped order
+ *   expert_offsets [E+1], kofs [E+1] (nvfp4moe_token_blocks)
+ *   Kp       K capacity (positions) of the outputs, a multiple of 64 and at
+ *            least 64 kofs[E]; 64 (ceil(R / 64) + E) always suffices
+ *   layout   NVFP4_W_ROWMAJOR: codes [C][Kp/2], bscales [C][Kp/16] (the
+ *            activation side of nvfp4_grouped_gemm_wgrad);
+ *            NVFP4_W_KTILED:   codes [Kp/64][C][32], bscales [Kp/64][C][4] (its
+ *            weight side)
+ *   rscales  float [E][C]
+ * Positions at or past 64 kofs[E] are not written.  Requires C % 256 == 0,
+ * 256 <= C <= 2^20.
+ *
+ * nvfp4_grouped_gemm_wgrad - dW_e = dequant(G_e^T) dequant(X_e^T)^T for every
+ * expert, exact products of the decoded values with FP32 accumulation (error
+ * within 2e-5 * sum |a w| per element), for all experts in one launch:
+ *   A (G side): row-major codes [M][Kp/2], bscales [M][Kp/16], rscales [E][M]
+ *   W (X side): K-tiled codes [Kp/64][N][32], bscales [Kp/64][N][4], rscales [E][N]
+ *   c          [E][M][N] of c_dtype: NVFP4_OUT_F32 (float) or NVFP4_OUT_BF16 (bf16 bits,
+ *              each FP32 result rounded to nearest even)
+ * Requires N % 16 == 0, 16 <= N <= 2^20, Kp % 64 == 0, M * Kp / 2 and
+ * N * Kp / 2 below 2^32, kofs[E] <= Kp / 64.
+ */
+#define NVFP4_IN_BF16 0
+#define NVFP4_IN_F32 1
+NVFP4MOE_API int nvfp4moe_token_blocks(const int32_t* expert_offsets, int32_t E, int32_t* kofs,
+                                       void* stream);
+NVFP4MOE_API int nvfp4_quantize_tokens(const void* x, int32_t x_dtype, int64_t x_rows, int64_t C,
+                                       const int32_t* row_to_tk, int32_t k,
+                                       const int32_t* expert_offsets, const int32_t* kofs, int32_t E,
+                                       int64_t Kp, int32_t layout, uint8_t* codes, uint8_t* bscales,
+                                       float* rscales, void* stream);
+NVFP4MOE_API int nvfp4_grouped_gemm_wgrad(const uint8_t* a_codes, const uint8_t* a_bscales,
+                                          const float* a_rscales, const uint8_t* w_codes,
+                                          const uint8_t* w_bscales, const float* w_rscales,
+                                          const int32_t* kofs, int32_t E, int64_t M, int64_t N,
+                                          int64_t Kp, void* c, int32_t c_dtype, void* stream);
+
+/*
  * swiglu_quantize - weighted SwiGLU of the gate_up output with the amax taken
  * on the fly, then NVFP4 quantisation of each routed row (for the down GEMM).
  *   gu        float [R_cap][2I]: gate = columns [0, I), up = columns [I, 2I)

@@ -43,13 +43,17 @@ def expert_slab(rows_f32, offsets, e: int, kofs) -> np.ndarray:
     return xs
 
 
-def quantize_tokens_ref(rows_f32, offsets):
-    """Per expert, the NVFP4 of X_e^T quantised along tokens.
+def quantize_expert_ref(rows_f32, offsets, e: int, kofs):
+    """The NVFP4 of X_e^T quantised along tokens: (codes [C][K_e/2], bscales [C][K_e/16], rscales [C])."""
+    return quantize_rows_f32(expert_slab(rows_f32, offsets, e, kofs))
 
-    Returns a list of (codes [C][K_e/2], bscales [C][K_e/16], rscales [C]) and kofs."""
+
+def quantize_tokens_ref(rows_f32, offsets):
+    """Per expert, the NVFP4 of X_e^T quantised along tokens: a list of
+    ``quantize_expert_ref`` results, and kofs."""
     kofs = token_blocks(offsets)
     E = len(offsets) - 1
-    return [quantize_rows_f32(expert_slab(rows_f32, offsets, e, kofs)) for e in range(E)], kofs
+    return [quantize_expert_ref(rows_f32, offsets, e, kofs) for e in range(E)], kofs
 
 
 def wgrad_ref(g_q, x_q):

@@ -70,6 +70,10 @@ SIGNATURES = {
     "nvfp4_grouped_gemm_swiglu": ([_P, _P, _P, _P, _I32, _I64, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _P,
                                    _c.c_size_t, _P], _c.c_int),
     "nvfp4_quantize_rows_f32": ([_P, _I64, _I64, _P, _I32, _P, _P, _P, _P], _c.c_int),
+    "nvfp4moe_token_blocks": ([_P, _I32, _P, _P], _c.c_int),
+    "nvfp4_quantize_tokens": ([_P, _I32, _I64, _I64, _P, _I32, _P, _P, _I32, _I64, _I32, _P, _P, _P, _P],
+                              _c.c_int),
+    "nvfp4_grouped_gemm_wgrad": ([_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _I32, _P], _c.c_int),
     "swiglu_quantize": ([_P, _I64, _I64, _P, _I32, _P, _P, _P, _P, _P, _P, _P], _c.c_int),
     "unpermute_combine": ([_P, _I64, _I32, _I64, _P, _P, _P, _P], _c.c_int),
     "permute_gather_bf16": ([_P, _I64, _I64, _I32, _P, _I32, _P, _P, _P], _c.c_int),
@@ -358,6 +362,80 @@ def nvfp4_quantize_rows_f32(x, expert_offsets=None, codes=None, bscales=None, rs
     _check("nvfp4_quantize_rows_f32", load_library().nvfp4_quantize_rows_f32(
         _ptr(x), rows, K, _ptr(expert_offsets), E, _ptr(codes), _ptr(bscales), _ptr(rscales), _stream()))
     return codes, bscales, rscales
+
+
+def token_blocks(expert_offsets, kofs=None):
+    """kofs [E+1] int32: the first 64-token step of each expert's slab along K."""
+    _req(expert_offsets, "expert_offsets", _I32T)
+    E = expert_offsets.numel() - 1
+    kofs = _empty((E + 1,), torch.int32, expert_offsets) if kofs is None else kofs
+    _req(kofs, "kofs", _I32T, numel=E + 1)
+    _check("nvfp4moe_token_blocks", load_library().nvfp4moe_token_blocks(
+        _ptr(expert_offsets), E, _ptr(kofs), _stream()))
+    return kofs
+
+
+def token_capacity(R: int, E: int) -> int:
+    """K positions that always hold every expert's padded slab."""
+    return 64 * (-(-R // 64) + E)
+
+
+def nvfp4_quantize_tokens(x, expert_offsets, kofs, Kp: int, layout: int = W_ROWMAJOR, row_to_tk=None, k: int = 1,
+                          out=None):
+    """Quantise along tokens, per expert: x [rows, C] (bf16 or f32; token order with
+    row_to_tk/k, else expert-grouped rows).  Returns (codes, bscales, rscales [E, C]):
+    row-major codes [C, Kp/2] / bscales [C, Kp/16], or K-tiled [Kp/64, C, 32] / [Kp/64, C, 4]."""
+    _req(x, "x", _BF16 + _F32, 2)
+    _req(expert_offsets, "expert_offsets", _I32T)
+    _req(row_to_tk, "row_to_tk", _I32T)
+    E = expert_offsets.numel() - 1
+    _req(kofs, "kofs", _I32T, numel=E + 1)
+    rows, C = x.shape
+    if row_to_tk is None and rows < 1:
+        raise ValueError("x has no rows")
+    o = out or {}
+    shp_c = (C, Kp // 2) if layout == W_ROWMAJOR else (Kp // 64, C, 32)
+    shp_b = (C, Kp // 16) if layout == W_ROWMAJOR else (Kp // 64, C, 4)
+    codes = o["codes"] if "codes" in o else _empty(shp_c, torch.uint8, x)
+    bsc = o["bscales"] if "bscales" in o else _empty(shp_b, torch.uint8, x)
+    rsc = o["rscales"] if "rscales" in o else _empty((E, C), torch.float32, x)
+    _req(codes, "codes", _U8, numel=C * Kp // 2); _req(bsc, "bscales", _U8, numel=C * Kp // 16)
+    _req(rsc, "rscales", _F32, numel=E * C)
+    dt = 1 if x.dtype == torch.float32 else 0
+    _check("nvfp4_quantize_tokens", load_library().nvfp4_quantize_tokens(
+        _ptr(x), dt, rows, C, _ptr(row_to_tk), k, _ptr(expert_offsets), _ptr(kofs), E, Kp, layout,
+        _ptr(codes), _ptr(bsc), _ptr(rsc), _stream()))
+    return codes, bsc, rsc
+
+
+def nvfp4_grouped_gemm_wgrad(a, w, kofs, c=None, out_dtype=None):
+    """dW [E, M, N] = per expert dequant(A_e) dequant(W_e)^T over its token slab,
+    float32 (default) or bfloat16 (out_dtype=torch.bfloat16, or a bf16 `c`).
+    a: row-major (codes [M, Kp/2], bscales [M, Kp/16], rscales [E, M]);
+    w: K-tiled (codes [Kp/64, N, 32], bscales [Kp/64, N, 4], rscales [E, N])."""
+    ac, ab, ar = a
+    wc, wb, wr = w
+    for t, n, d in ((ac, "a_codes", _U8), (ab, "a_bscales", _U8), (ar, "a_rscales", _F32),
+                    (wc, "w_codes", _U8), (wb, "w_bscales", _U8), (wr, "w_rscales", _F32), (kofs, "kofs", _I32T)):
+        _req(t, n, d)
+    M, half = ac.shape
+    Kp = half * 2
+    E = kofs.numel() - 1
+    if wc.dim() != 3 or wc.shape[0] != Kp // 64 or wc.shape[2] != 32:
+        raise ValueError("w codes must be K-tiled [Kp/64, N, 32] over the same Kp")
+    N = wc.shape[1]
+    _req(ab, "a_bscales", _U8, numel=M * Kp // 16); _req(ar, "a_rscales", _F32, numel=E * M)
+    _req(wb, "w_bscales", _U8, numel=N * Kp // 16); _req(wr, "w_rscales", _F32, numel=E * N)
+    if out_dtype is None:
+        out_dtype = torch.float32 if c is None or c.dtype == torch.float32 else torch.bfloat16
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    c = _empty((E, M, N), out_dtype, ac) if c is None else c
+    _req(c, "c", _F32 if out_dtype == torch.float32 else _BF16, numel=E * M * N)
+    _check("nvfp4_grouped_gemm_wgrad", load_library().nvfp4_grouped_gemm_wgrad(
+        _ptr(ac), _ptr(ab), _ptr(ar), _ptr(wc), _ptr(wb), _ptr(wr), _ptr(kofs), E, M, N, Kp, _ptr(c),
+        OUT_F32 if out_dtype == torch.float32 else OUT_BF16, _stream()))
+    return c
 
 
 def swiglu_quantize(gu, expert_offsets, topk_w=None, row_to_tk=None, h_out=False, out=None):

@@ -179,6 +179,7 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // One tile: rows [m0, m0 + rows) of expert e (rows <= BM), columns [n0, n0 + BN).
 struct Tile {
   int e, m0, rows, n0;
+  int kb0, nk;   // first K-step of the tile's contraction and its K-steps
 };
 
 // the expert of m-tile tm: the last e with tile_start[e] <= tm
@@ -192,17 +193,35 @@ __device__ __forceinline__ int expert_of(int tm, const int* tile_start, int E) {
 }
 
 // mt_expert: the prologue's table of expert_of, or null when it did not fit
+// Row groups: rows [offsets[e], offsets[e+1]) of group e; with KG (K-grouped,
+// the weight gradient) every group has Mg rows (offsets unused) and contracts
+// over its own K-steps [kofs[e], kofs[e+1]).
+template <bool KG>
+__device__ __forceinline__ int group_off(const int32_t* __restrict__ offsets, int Mg, int e) {
+  if constexpr (KG) return e * Mg;
+  else return offsets[e];
+}
+
+template <bool KG>
 __device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_start,
                                         const int16_t* mt_expert, int E,
-                                        const int32_t* __restrict__ offsets) {
+                                        const int32_t* __restrict__ offsets, int Mg,
+                                        const int32_t* __restrict__ kofs, int nk) {
   const int tm = L / n_tiles, tn = L - tm * n_tiles;
   const int lo = mt_expert ? (int)mt_expert[tm] : expert_of(tm, tile_start, E);
   // the values are the same in every lane: keep them in scalar registers
   Tile t;
   t.e = __builtin_amdgcn_readfirstlane(lo);
-  t.m0 = __builtin_amdgcn_readfirstlane(offsets[t.e] + (tm - tile_start[t.e]) * BM);
-  t.rows = __builtin_amdgcn_readfirstlane(min(BM, offsets[t.e + 1] - t.m0));
+  t.m0 = __builtin_amdgcn_readfirstlane(group_off<KG>(offsets, Mg, t.e) + (tm - tile_start[t.e]) * BM);
+  t.rows = __builtin_amdgcn_readfirstlane(min(BM, group_off<KG>(offsets, Mg, t.e + 1) - t.m0));
   t.n0 = tn * BN;
+  if constexpr (KG) {
+    t.kb0 = __builtin_amdgcn_readfirstlane(kofs[t.e]);
+    t.nk = __builtin_amdgcn_readfirstlane(kofs[t.e + 1] - t.kb0);
+  } else {
+    t.kb0 = 0;
+    t.nk = nk;
+  }
   return t;
 }
 
@@ -225,15 +244,22 @@ __device__ __forceinline__ float swiglu_f32(float g, float u, float w) {
 // fragment 0 holds gate rows 256 tn + 32 w + (0..31) and fragment 1 the up rows
 // I + 256 tn + 32 w + (0..31), so a lane holds g and u of the same (row,
 // column) in acc[i][0] and acc[i][1].
-template <bool KT, bool OB, bool SW>
+// KG: K-grouped (the weight gradient): group e is the Mg activation rows
+// (row-major [Mg][K/2], K = the padded total of all groups' K-steps) times the
+// K-tiled weights [K/64][N][32], both over the group's K-steps
+// [kofs[e], kofs[e+1]); its output rows are e Mg .. e Mg + Mg - 1; row scales
+// a_rscales [E][Mg], w_rscales [E][N].
+template <bool KT, bool OB, bool SW, bool KG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_bscales,
     const float* __restrict__ a_rscales, const int32_t* __restrict__ offsets, int E,
     const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_bscales,
     const float* __restrict__ w_rscales, int N, int K, void* __restrict__ c,
-    const float* __restrict__ w_rows, float* __restrict__ gu_out, int I) {
+    const float* __restrict__ w_rows, float* __restrict__ gu_out, int I,
+    const int32_t* __restrict__ kofs, int Mg) {
   static_assert(!SW || (KT && !OB), "the SwiGLU epilogue reads K-tiled weights and writes FP32");
+  static_assert(!KG || (KT && !SW), "K-grouped tiles read K-tiled weights");
   __shared__ Smem sm;
   constexpr bool w_tiled = KT;
 
@@ -246,7 +272,7 @@ void grouped_gemm_kernel(
     int carry = 0;
     for (int e0 = 0; e0 < E; e0 += kWave) {
       const int e = e0 + lane;
-      const int v = e < E ? (offsets[e + 1] - offsets[e] + BM - 1) / BM : 0;
+      const int v = e < E ? (group_off<KG>(offsets, Mg, e + 1) - group_off<KG>(offsets, Mg, e) + BM - 1) / BM : 0;
       int incl = v;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
@@ -299,7 +325,7 @@ void grouped_gemm_kernel(
   // rows or 64 scale dwords.  Activation rows: lane l -> row l/2, 16-byte half
   // l%2 (row-major).  Weight rows: lane l -> row l%32, half l/32, so that a
   // fragment read (16 lanes: 16 rows, one half) covers 256 contiguous bytes.
-  int lL = begin, lk = 0;
+  int lL = begin, lk = 0, nkl = nk;   // the loaded tile's K-steps
   uint32_t off_c[kCIW], off_s[kSIW];
   // Weight K-step strides: row-major [E][N][K/2] moves 32 code bytes (4 scale
   // bytes) along a row per K-step; the K-tiled layout [E][K/64][N][32] moves
@@ -333,20 +359,26 @@ void grouped_gemm_kernel(
     else return min(t.n0 + c, cap);
   };
   auto set_load_tile = [&](int L) __attribute__((always_inline)) {
-    const Tile t = tile_at(L, n_tiles, sm.tile_start, mt_tab, E, offsets);
+    const Tile t = tile_at<KG>(L, n_tiles, sm.tile_start, mt_tab, E, offsets, Mg, kofs, nk);
+    nkl = t.nk;
     if constexpr (KT) {
       const int m_last = t.m0 + t.rows - 1;
       const uint32_t half16 = (lane & 1) * 16;
-      const uint32_t wbase = (uint32_t)t.e * nk * N;
+      // K-grouped: activation rows are the group's local rows, and both
+      // operands start at the group's first K-step
+      const int a_row0 = KG ? t.e * Mg : 0;
+      const uint32_t a_k0 = (uint32_t)t.kb0 * kRowB, as_k0 = (uint32_t)t.kb0 * kScB;
+      const uint32_t wbase = KG ? (uint32_t)t.kb0 * N : (uint32_t)t.e * nk * N;
       auto wrow = [&](int q) __attribute__((always_inline)) {
         const uint32_t n = (uint32_t)wcol(t, 32 * (q - BM / 32) + (lane & 31), N - 1);
         return (wbase + n) * kRowB + (lane >> 5) * 16;
       };
-      vo0 = wave < 4 ? (uint32_t)min(t.m0 + 32 * wave + (lane >> 1), m_last) * kb + half16 : wrow(wave);
+      vo0 = wave < 4 ? (uint32_t)(min(t.m0 + 32 * wave + (lane >> 1), m_last) - a_row0) * kb + a_k0 + half16
+                     : wrow(wave);
       vo1 = wrow(wave + 8);
       if (wave < 4) vo2 = wrow(wave + 16);
       else if (wave < 6) vo2 = (wbase + (uint32_t)wcol(t, 256 * (wave - 4) + 4 * lane, N - 4)) * kScB;
-      else vo2 = (uint32_t)min(t.m0 + 64 * (wave - 6) + lane, m_last) * ks;
+      else vo2 = (uint32_t)(min(t.m0 + 64 * (wave - 6) + lane, m_last) - a_row0) * ks + as_k0;
       return;
     }
     const int m_last = t.m0 + t.rows - 1;
@@ -384,7 +416,7 @@ void grouped_gemm_kernel(
       lds_dma16_at(w_codes, (uint32_t)lk * step1 + vo1, ls + ldo1);
       if (wave < 6) lds_dma16_at(src2, (uint32_t)lk * step2 + vo2, ls + ldo2);
       else lds_dma4_at(src2, (uint32_t)lk * step2 + vo2, ls + ldo2);
-      if (++lk == nk) {
+      if (++lk == nkl) {
         lk = 0;
         lL += step;
         if (lL < end) set_load_tile(lL);
@@ -405,7 +437,7 @@ void grouped_gemm_kernel(
       if (q < 2) lds_dma4(a_bscales, kss + off_s[u], S.as + q * 256);
       else if (q < kSI) lds_dma4(w_bscales, kws + off_s[u], S.as + q * 256);
     }
-    if (++lk == nk) {
+    if (++lk == nkl) {
       lk = 0;
       lL += step;
       if (lL < end) set_load_tile(lL);
@@ -713,10 +745,10 @@ void grouped_gemm_kernel(
     mma_step(full_tag, fa_eff);   // K-step 0: its wait, barrier and loads are done by the caller
     sc = sc == kStages - 1 ? 0 : sc + 1;
     ab ^= 1;
-    for (int kt = 1; kt < nk; ++kt) {
+    for (int kt = 1; kt < t.nk; ++kt) {
       wait_vmcnt(n_last);
       lds_barrier();
-      if (kt == nk - 1) issue_rscales(t, rbuf);
+      if (kt == t.nk - 1) issue_rscales(t, rbuf);
       n_last = issue_loads(sm.st[sc]);
       mma_step(full_tag, fa_eff);
       sc = sc == kStages - 1 ? 0 : sc + 1;
@@ -726,12 +758,12 @@ void grouped_gemm_kernel(
 
   Tile prev{0, 0, 0, 0};
   for (int L = begin; L < end; L += step) {
-    const Tile t = tile_at(L, n_tiles, sm.tile_start, mt_tab, E, offsets);
+    const Tile t = tile_at<KG>(L, n_tiles, sm.tile_start, mt_tab, E, offsets, Mg, kofs, nk);
     const int fa_eff = (t.rows + 31) >> 5;
     wait_vmcnt(n_last);
     lds_barrier();
     epilogue(prev, rbuf ^ 1);   // before the first tile: no rows, every store is dropped
-    if (nk == 1) issue_rscales(t, rbuf);
+    if (t.nk == 1) issue_rscales(t, rbuf);
     n_last = issue_loads(sm.st[sc]);
     if (fa_eff == FA) run_tile(std::true_type{}, FA, t);
     else run_tile(std::false_type{}, fa_eff, t);
@@ -779,9 +811,9 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uin
   if (grid >= 8) grid &= ~7ll;
   hipStream_t s = static_cast<hipStream_t>(stream);
 #define GG_LAUNCH(KT, OB)                                                                    \
-  g5::grouped_gemm_kernel<KT, OB, false><<<(unsigned)grid, g5::kThreads, 0, s>>>(             \
+  g5::grouped_gemm_kernel<KT, OB, false, false><<<(unsigned)grid, g5::kThreads, 0, s>>>(      \
       a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales, (int)N, \
-      (int)K, c, nullptr, nullptr, 0)
+      (int)K, c, nullptr, nullptr, 0, nullptr, 0)
   const bool kt = w_layout == NVFP4_W_KTILED, ob = c_dtype == NVFP4_OUT_BF16;
   if (kt && !ob) GG_LAUNCH(true, false);
   else if (kt) GG_LAUNCH(true, true);
@@ -838,8 +870,41 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm_swiglu(
     gather_row_weights_kernel<<<(unsigned)((R_cap + 255) / 256), 256, 0, s>>>(
         topk_w, row_to_tk, expert_offsets, E, R_cap, w_rows);
   }
-  g5::grouped_gemm_kernel<true, false, true><<<(unsigned)grid, g5::kThreads, 0, s>>>(
+  g5::grouped_gemm_kernel<true, false, true, false><<<(unsigned)grid, g5::kThreads, 0, s>>>(
       a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales,
-      (int)(2 * I), (int)K, h, w_rows, gu, (int)I);
+      (int)(2 * I), (int)K, h, w_rows, gu, (int)I, nullptr, 0);
+  return launch_status();
+}
+
+extern "C" NVFP4MOE_API int nvfp4_grouped_gemm_wgrad(
+    const uint8_t* a_codes, const uint8_t* a_bscales, const float* a_rscales,
+    const uint8_t* w_codes, const uint8_t* w_bscales, const float* w_rscales,
+    const int32_t* kofs, int32_t E, int64_t M, int64_t N, int64_t Kp, void* c, int32_t c_dtype,
+    void* stream) {
+  if (c_dtype != NVFP4_OUT_F32 && c_dtype != NVFP4_OUT_BF16) return NVFP4_ERR_ARG;
+  if (E < 1 || E > NVFP4MOE_MAX_EXPERTS || M < 1 || N < 16 || N % 16 != 0 || N > (1 << 20))
+    return NVFP4_ERR_SHAPE;
+  if (Kp <= 0 || Kp % g5::BK != 0) return NVFP4_ERR_SHAPE;
+  if ((int64_t)E * M > INT32_MAX / 2 || (int64_t)E * N > INT32_MAX) return NVFP4_ERR_SHAPE;
+  // 32-bit byte offsets into each operand
+  if (M * (Kp / 2) > (int64_t)UINT32_MAX || N * (Kp / 2) > (int64_t)UINT32_MAX) return NVFP4_ERR_SHAPE;
+  if (!a_codes || !a_bscales || !a_rscales || !w_codes || !w_bscales || !w_rscales || !kofs || !c)
+    return NVFP4_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(a_bscales) || !aligned16(a_rscales) ||
+      !aligned16(w_codes) || !aligned16(w_bscales) || !aligned16(w_rscales) || !aligned16(c))
+    return NVFP4_ERR_ALIGN;
+  const int64_t max_tiles = (int64_t)E * ((M + g5::BM - 1) / g5::BM) * ((N + g5::BN - 1) / g5::BN);
+  if (max_tiles > INT32_MAX) return NVFP4_ERR_SHAPE;
+  int64_t grid = max_tiles < 256 ? max_tiles : 256;
+  if (grid >= 8) grid &= ~7ll;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (c_dtype == NVFP4_OUT_BF16)
+    g5::grouped_gemm_kernel<true, true, false, true><<<(unsigned)grid, g5::kThreads, 0, s>>>(
+        a_codes, a_bscales, a_rscales, nullptr, E, w_codes, w_bscales, w_rscales, (int)N, (int)Kp, c,
+        nullptr, nullptr, 0, kofs, (int)M);
+  else
+    g5::grouped_gemm_kernel<true, false, false, true><<<(unsigned)grid, g5::kThreads, 0, s>>>(
+        a_codes, a_bscales, a_rscales, nullptr, E, w_codes, w_bscales, w_rscales, (int)N, (int)Kp, c,
+        nullptr, nullptr, 0, kofs, (int)M);
   return launch_status();
 }

@@ -765,6 +765,125 @@ __global__ __launch_bounds__(256) void quantize_rows_f32_kernel(
   store_row<NCH>(o, sw, K, r, codes, bscales, rscales);
 }
 
+// ------------------------------------------------------------------ quantisation along tokens
+// The token blocks of the weight gradient: kofs[e] = the first 64-token step of
+// expert e's slab, each expert taking max(1, ceil(rows / 64)) steps.  One
+// workgroup (E <= 1024).
+__global__ __launch_bounds__(1024) void token_blocks_kernel(const int32_t* __restrict__ offsets, int E,
+                                                            int32_t* __restrict__ kofs) {
+  __shared__ int32_t wsum[16];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int v = tid < E ? max(1, (offsets[tid + 1] - offsets[tid] + 63) >> 6) : 0;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  if (tid < E) kofs[tid] = before + incl - v;
+  if (tid == E - 1) kofs[E] = before + incl;
+}
+
+// Workgroup (column chunk, expert e): 256 columns c0 .. c0 + 255 of the
+// expert's rows, thread (cg = tid % 32, rg = tid / 32) on the 8 columns
+// c0 + 8 cg .. +7.  Pass 1: column maxima over the expert's rows (row groups
+// rg, rg + 8, ...), combined in LDS; s = amax / 2688 per column.  Pass 2: per
+// block of 16 tokens (blocks rg, rg + 8, ...) the 16 x 8 values, each
+// column's block scale and codes by the row quantiser's arithmetic, written
+// as 8 code bytes and one scale byte per column; blocks past the expert's
+// rows are zero padding (scale 0, codes 0).
+template <bool F32IN, bool KTILED>
+__global__ __launch_bounds__(256) void quantize_tokens_kernel(
+    const void* __restrict__ x, int64_t x_rows, int C, const int32_t* __restrict__ row_to_tk, int k,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ kofs, int64_t Kp,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales, float* __restrict__ rscales) {
+  __shared__ float cmax[8][256];
+  const int tid = threadIdx.x, cg = tid & 31, rg = tid >> 5;
+  const int e = blockIdx.y;
+  const int c = (int)blockIdx.x * 256 + 8 * cg;                  // first of the thread's 8 columns
+  const int r0 = offsets[e], n = offsets[e + 1] - r0;
+  const int kb0 = kofs[e], nblk = (kofs[e + 1] - kb0) * 4;      // blocks of 16 tokens in the slab
+  if ((int64_t)(kofs[e + 1]) * 64 > Kp) return;                  // slab outside the buffer: skipped
+  auto load8 = [&](int r, float (&v)[8]) __attribute__((always_inline)) {
+    int64_t xr = r0 + r;
+    if (row_to_tk) xr = row_to_tk[xr] / k;
+    xr = xr < 0 ? 0 : (xr >= x_rows ? x_rows - 1 : xr);
+    if constexpr (F32IN) {
+      const float* p = static_cast<const float*>(x) + xr * C + c;
+      const float4 a = *reinterpret_cast<const float4*>(p);
+      const float4 b = *reinterpret_cast<const float4*>(p + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + xr * C + c);
+      v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+      v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+    }
+  };
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r = rg; r < n; r += 8) {
+    float v[8];
+    load8(r, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m[j] = fmaxf(m[j], __builtin_fabsf(v[j]));
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) cmax[rg][8 * cg + j] = m[j];
+  __syncthreads();
+  float s[8], six_s[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float a = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) a = fmaxf(a, cmax[g][8 * cg + j]);
+    s[j] = a / 2688.0f;
+    six_s[j] = 6.0f * s[j];
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rscales[(int64_t)e * C + c + j] = s[j];
+  }
+  for (int b = rg; b < nblk; b += 8) {
+    float v[16][8];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (16 * b + i < n) load8(16 * b + i, v[i]);
+      else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[i][j] = 0.0f;
+      }
+    }
+    const int64_t kpos = (int64_t)kb0 * 64 + 16 * b;             // first token position of the block
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float col[16];
+      float bm = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        col[i] = v[i][j];
+        bm = fmaxf(bm, __builtin_fabsf(col[i]));
+      }
+      const uint32_t bs = s[j] != 0.0f ? e4m3_encode_nonneg(bm / six_s[j]) : 0u;
+      const float d = e4m3_decode_nonneg(bs) * s[j];
+      uint32_t w0, w1;
+      block_codes16(col, d, bm, w0, w1);
+      const int64_t row = c + j;
+      if constexpr (KTILED) {
+        const int64_t slab = kpos >> 6;
+        const int q = (int)(kpos & 63) >> 4;                     // block within the slab
+        *reinterpret_cast<uint2*>(codes + (slab * C + row) * 32 + 8 * q) = make_uint2(w0, w1);
+        bscales[(slab * C + row) * 4 + q] = (uint8_t)bs;
+      } else {
+        *reinterpret_cast<uint2*>(codes + row * (Kp / 2) + kpos / 2) = make_uint2(w0, w1);
+        bscales[row * (Kp / 16) + kpos / 16] = (uint8_t)bs;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ dispatch
 inline int nch_for(int64_t K) {
   return K <= 512 ? 1 : K <= 1024 ? 2 : K <= 2048 ? 4 : K <= 4096 ? 8 : 16;
@@ -876,6 +995,41 @@ NVFP4MOE_API int nvfp4_quantize_rows_f32(const float* x, int64_t rows, int64_t K
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   NVFP4_DISPATCH_NCH(K, quantize_rows_f32_kernel, grid, s, x, rows, (int)K, expert_offsets, E, codes,
                      bscales, rscales);
+  return launch_status();
+}
+
+NVFP4MOE_API int nvfp4moe_token_blocks(const int32_t* expert_offsets, int32_t E, int32_t* kofs,
+                                       void* stream) {
+  if (E < 1 || E > NVFP4MOE_MAX_EXPERTS) return NVFP4_ERR_SHAPE;
+  if (!expert_offsets || !kofs) return NVFP4_ERR_NULL;
+  token_blocks_kernel<<<1, 1024, 0, static_cast<hipStream_t>(stream)>>>(expert_offsets, E, kofs);
+  return launch_status();
+}
+
+NVFP4MOE_API int nvfp4_quantize_tokens(const void* x, int32_t x_dtype, int64_t x_rows, int64_t C,
+                                       const int32_t* row_to_tk, int32_t k,
+                                       const int32_t* expert_offsets, const int32_t* kofs, int32_t E,
+                                       int64_t Kp, int32_t layout, uint8_t* codes, uint8_t* bscales,
+                                       float* rscales, void* stream) {
+  if (x_dtype != NVFP4_IN_BF16 && x_dtype != NVFP4_IN_F32) return NVFP4_ERR_ARG;
+  if (layout != NVFP4_W_ROWMAJOR && layout != NVFP4_W_KTILED) return NVFP4_ERR_ARG;
+  if (E < 1 || E > NVFP4MOE_MAX_EXPERTS || x_rows < 1 || C < 256 || C % 256 != 0 || C > (1 << 20))
+    return NVFP4_ERR_SHAPE;
+  if (Kp <= 0 || Kp % 64 != 0 || (row_to_tk && (k < 1 || k > NVFP4MOE_MAX_TOPK))) return NVFP4_ERR_SHAPE;
+  if (!x || !expert_offsets || !kofs || !codes || !bscales || !rscales) return NVFP4_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(bscales) || !aligned16(rscales))
+    return NVFP4_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(C / 256), (unsigned)E);
+#define QT_LAUNCH(F, KTL)                                                                         \
+  quantize_tokens_kernel<F, KTL><<<grid, 256, 0, s>>>(x, x_rows, (int)C, row_to_tk, k, expert_offsets, \
+                                                     kofs, Kp, codes, bscales, rscales)
+  const bool f32 = x_dtype == NVFP4_IN_F32, kt = layout == NVFP4_W_KTILED;
+  if (f32 && kt) QT_LAUNCH(true, true);
+  else if (f32) QT_LAUNCH(true, false);
+  else if (kt) QT_LAUNCH(false, true);
+  else QT_LAUNCH(false, false);
+#undef QT_LAUNCH
   return launch_status();
 }
 
