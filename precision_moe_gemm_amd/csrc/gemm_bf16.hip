@@ -342,12 +342,17 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
   // splits evenly), columns 16j + 4g .. +3 of the wavefront's 64; rows past the tile's rows and
   // columns past N are not written.  The accumulators are cleared.
   auto epilogue = [&](const Tile& t) __attribute__((always_inline)) {
+    // the lane's position, recomputed here: a value carried from the prologue
+    // would hold a register through the K-loop (which has none to spare)
+    int le;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(le));
+    const int l16e = le & 15, ge = le >> 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int r = 32 * i + 16 * wm + l16;
+      const int r = 32 * i + 16 * wm + l16e;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int n = t.n0 + WN * wn + 16 * j + 4 * g;
+        const int n = t.n0 + WN * wn + 16 * j + 4 * ge;
         if (r < t.rows && n < N)
           *reinterpret_cast<floatx4*>(c + (int64_t)(t.m0 + r) * N + n) = acc[i][j];
         acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
