@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void unpermute_combine_kernel(
         const int sl = s0 + u;                       // < 40: a lane index
         const int row = __shfl(my_row, sl, kWave);
         wv[u] = __shfl(my_w, sl, kWave);
-        ok[u] = sl < k && row >= 0 && inside;
+        ok[u] = sl < k && row >= 0 && row < T * k && inside;   // rows of d: T * k
         v[u] = ok[u] ? *reinterpret_cast<const float4*>(d + (int64_t)row * H + base)
                      : make_float4(0.f, 0.f, 0.f, 0.f);
       }
@@ -62,11 +62,11 @@ __global__ __launch_bounds__(256) void unpermute_combine_kernel(
 
 // out[r] = x[row_to_tk[r] / k] for every routed row r.
 __global__ __launch_bounds__(256) void permute_gather_kernel(
-    const uint16_t* __restrict__ x, int H, int k, const int32_t* __restrict__ offsets, int E,
+    const uint16_t* __restrict__ x, int64_t T, int H, int k, const int32_t* __restrict__ offsets, int E,
     const int32_t* __restrict__ row_to_tk, uint16_t* __restrict__ out) {
   const int64_t r = (int64_t)blockIdx.x * kRows + (threadIdx.x >> 6);
-  if (r >= offsets[E]) return;
-  const int64_t t = row_to_tk[r] / k;
+  if (r >= offsets[E] || r >= T * k) return;
+  const int64_t t = min(max((int64_t)(row_to_tk[r] / k), (int64_t)0), T - 1);   // a bad map entry stays in x
   const uint16_t* src = x + t * (int64_t)H;
   uint16_t* dst = out + r * (int64_t)H;
   for (int base = lane_id() * 8; base < H; base += kWave * 8)
@@ -76,12 +76,16 @@ __global__ __launch_bounds__(256) void permute_gather_kernel(
 // Gradient of h = w * silu(g) * u in float64 (sigmoid from a refined
 // reciprocal, silu = g * sigmoid), each output rounded once to bf16.
 __global__ __launch_bounds__(256) void swiglu_backward_kernel(
-    const float* __restrict__ gu, const float* __restrict__ dh, int I,
+    const float* __restrict__ gu, const float* __restrict__ dh, int64_t R_cap, int I,
     const int32_t* __restrict__ offsets, int E, const float* __restrict__ topk_w,
     const int32_t* __restrict__ row_to_tk, uint16_t* __restrict__ dgu) {
   const int64_t r = (int64_t)blockIdx.x * kRows + (threadIdx.x >> 6);
-  if (r >= offsets[E]) return;
-  const float w = topk_w ? topk_w[row_to_tk[r]] : 1.0f;
+  if (r >= offsets[E] || r >= R_cap) return;
+  float w = 1.0f;
+  if (topk_w) {   // the router weight of the row's (token, slot); a bad map entry gives 0
+    const int32_t i = row_to_tk[r];
+    w = (i >= 0 && i < R_cap) ? topk_w[i] : 0.0f;
+  }
   const float* grow = gu + r * (int64_t)(2 * I);
   const float* drow = dh + r * (int64_t)I;
   uint16_t* orow = dgu + r * (int64_t)(2 * I);
@@ -182,7 +186,7 @@ NVFP4MOE_API int permute_gather_bf16(const uint16_t* x, int64_t T, int64_t H, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t R_cap = T * k;
   permute_gather_kernel<<<(unsigned)((R_cap + kRows - 1) / kRows), 256, 0, s>>>(
-      x, (int)H, k, expert_offsets, E, row_to_tk, out);
+      x, T, (int)H, k, expert_offsets, E, row_to_tk, out);
   return launch_status();
 }
 
@@ -197,7 +201,7 @@ NVFP4MOE_API int swiglu_backward(const float* gu, const float* dh, int64_t R_cap
   if (!aligned16(gu) || !aligned16(dh) || !aligned16(dgu)) return NVFP4_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   swiglu_backward_kernel<<<(unsigned)((R_cap + kRows - 1) / kRows), 256, 0, s>>>(
-      gu, dh, (int)I, expert_offsets, E, topk_w, row_to_tk, dgu);
+      gu, dh, R_cap, (int)I, expert_offsets, E, topk_w, row_to_tk, dgu);
   return launch_status();
 }
 

@@ -126,8 +126,14 @@ struct Tile {
   int e, m0, rows, n0;
 };
 
+// expert offsets clamped into [0, Rc] (the rows of the output buffer): malformed
+// offsets give wrong rows but no access outside the buffers
+__device__ __forceinline__ int off_at(const int32_t* __restrict__ offsets, int Rc, int e) {
+  return min(max(offsets[e], 0), Rc);
+}
+
 __device__ __forceinline__ Tile tile_at(int L, int n_tiles, int bm, const int* tile_start, int E,
-                                        const int32_t* __restrict__ offsets) {
+                                        const int32_t* __restrict__ offsets, int Rc) {
   const int tm = L / n_tiles, tn = L - tm * n_tiles;
   int lo = 0, hi = E;
   while (hi - lo > 1) {
@@ -136,8 +142,8 @@ __device__ __forceinline__ Tile tile_at(int L, int n_tiles, int bm, const int* t
   }
   Tile t;
   t.e = __builtin_amdgcn_readfirstlane(lo);
-  t.m0 = __builtin_amdgcn_readfirstlane(offsets[t.e] + (tm - tile_start[t.e]) * bm);
-  t.rows = __builtin_amdgcn_readfirstlane(min(bm, offsets[t.e + 1] - t.m0));
+  t.m0 = __builtin_amdgcn_readfirstlane(off_at(offsets, Rc, t.e) + (tm - tile_start[t.e]) * bm);
+  t.rows = __builtin_amdgcn_readfirstlane(min(bm, off_at(offsets, Rc, t.e + 1) - t.m0));
   t.n0 = tn * BN;
   return t;
 }
@@ -146,7 +152,7 @@ template <bool KN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __restrict__ a_map,
                               int a_div, int a_rows, const int32_t* __restrict__ offsets,
-                              int E, const uint16_t* __restrict__ w, int N, int K,
+                              int E, int Rc, const uint16_t* __restrict__ w, int N, int K,
                               float* __restrict__ c) {
   constexpr int kAF = BM / 16;                      // A load instructions per K-step (16 rows each)
   constexpr int kAI = (kAF + kWaves - 1) / kWaves;  // ... per wavefront, at most
@@ -175,7 +181,7 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
       int mt = 0;
       for (int e0 = 0; e0 < E; e0 += kWave) {
         const int e = e0 + lane;
-        int v = e < E ? (offsets[e + 1] - offsets[e] + h - 1) / h : 0;
+        int v = e < E ? max(0, off_at(offsets, Rc, e + 1) - off_at(offsets, Rc, e) + h - 1) / h : 0;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
         mt += v;
@@ -191,7 +197,7 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
     int carry = 0;
     for (int e0 = 0; e0 < E; e0 += kWave) {
       const int e = e0 + lane;
-      const int v = e < E ? (offsets[e + 1] - offsets[e] + best - 1) / best : 0;
+      const int v = e < E ? max(0, off_at(offsets, Rc, e + 1) - off_at(offsets, Rc, e) + best - 1) / best : 0;
       int incl = v;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
@@ -237,7 +243,7 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
   uint32_t off_a[kAI], off_w[kWI];
   int na = 0;   // A instructions of this wavefront for the load tile: q = wave + 8u < ceil(rows / 16)
   auto set_load_tile = [&](int L) __attribute__((always_inline)) {
-    const Tile t = tile_at(L, n_tiles, bm, sm.tile_start, E, offsets);
+    const Tile t = tile_at(L, n_tiles, bm, sm.tile_start, E, offsets, Rc);
     const int fa = min(kAF, (t.rows + 15) >> 4);
     na = fa > wave ? (fa - wave + kWaves - 1) / kWaves : 0;
 #pragma unroll
@@ -393,7 +399,7 @@ void bf16_grouped_gemm_kernel(const uint16_t* __restrict__ a, const int32_t* __r
 
   Tile prev{0, 0, 0, 0};
   for (int L = begin; L < end; L += step) {
-    const Tile t = tile_at(L, n_tiles, bm, sm.tile_start, E, offsets);
+    const Tile t = tile_at(L, n_tiles, bm, sm.tile_start, E, offsets, Rc);
     top();
     epilogue(prev);   // before the first tile: no rows, nothing is written
     const int fm_eff = min(FM, (((t.rows + 15) >> 4) - wm + 1) >> 1);
@@ -438,10 +444,10 @@ int launch_bf16_grouped_gemm(const uint16_t* a, int64_t a_rows, const int32_t* a
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (w_layout == NVFP4MOE_W_KN)
     gb::bf16_grouped_gemm_kernel<true><<<(unsigned)grid, gb::kThreads, 0, s>>>(
-        a, a_map, a_div, (int)a_rows, expert_offsets, E, w, (int)N, (int)K, c);
+        a, a_map, a_div, (int)a_rows, expert_offsets, E, (int)R_cap, w, (int)N, (int)K, c);
   else
     gb::bf16_grouped_gemm_kernel<false><<<(unsigned)grid, gb::kThreads, 0, s>>>(
-        a, a_map, a_div, (int)a_rows, expert_offsets, E, w, (int)N, (int)K, c);
+        a, a_map, a_div, (int)a_rows, expert_offsets, E, (int)R_cap, w, (int)N, (int)K, c);
   return launch_status();
 }
 

@@ -193,13 +193,15 @@ __device__ __forceinline__ int expert_of(int tm, const int* tile_start, int E) {
 }
 
 // mt_expert: the prologue's table of expert_of, or null when it did not fit
-// Row groups: rows [offsets[e], offsets[e+1]) of group e; with KG (K-grouped,
-// the weight gradient) every group has Mg rows (offsets unused) and contracts
-// over its own K-steps [kofs[e], kofs[e+1]).
+// Row groups: rows [offsets[e], offsets[e+1]) of group e, each offset clamped
+// into [0, Rc] (the rows the buffers hold), so that malformed offsets give
+// wrong rows but no access outside the buffers; with KG (K-grouped, the weight
+// gradient) every group has Mg rows (offsets unused) and contracts over its own
+// K-steps [kofs[e], kofs[e+1]), clamped into the nk K-steps of the operands.
 template <bool KG>
 __device__ __forceinline__ int group_off(const int32_t* __restrict__ offsets, int Mg, int e) {
   if constexpr (KG) return e * Mg;
-  else return offsets[e];
+  else return min(max(offsets[e], 0), Mg);
 }
 
 template <bool KG>
@@ -216,8 +218,8 @@ __device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_star
   t.rows = __builtin_amdgcn_readfirstlane(min(BM, group_off<KG>(offsets, Mg, t.e + 1) - t.m0));
   t.n0 = tn * BN;
   if constexpr (KG) {
-    t.kb0 = __builtin_amdgcn_readfirstlane(kofs[t.e]);
-    t.nk = __builtin_amdgcn_readfirstlane(kofs[t.e + 1] - t.kb0);
+    t.kb0 = __builtin_amdgcn_readfirstlane(min(max(kofs[t.e], 0), nk - 1));
+    t.nk = __builtin_amdgcn_readfirstlane(min(max(kofs[t.e + 1] - t.kb0, 1), nk - t.kb0));
   } else {
     t.kb0 = 0;
     t.nk = nk;
@@ -244,6 +246,8 @@ __device__ __forceinline__ float swiglu_f32(float g, float u, float w) {
 // fragment 0 holds gate rows 256 tn + 32 w + (0..31) and fragment 1 the up rows
 // I + 256 tn + 32 w + (0..31), so a lane holds g and u of the same (row,
 // column) in acc[i][0] and acc[i][1].
+// Mg: the row capacity R_cap of A and C (offsets are clamped into it), or with
+// KG the rows of every group.
 // KG: K-grouped (the weight gradient): group e is the Mg activation rows
 // (row-major [Mg][K/2], K = the padded total of all groups' K-steps) times the
 // K-tiled weights [K/64][N][32], both over the group's K-steps
@@ -272,7 +276,8 @@ void grouped_gemm_kernel(
     int carry = 0;
     for (int e0 = 0; e0 < E; e0 += kWave) {
       const int e = e0 + lane;
-      const int v = e < E ? (group_off<KG>(offsets, Mg, e + 1) - group_off<KG>(offsets, Mg, e) + BM - 1) / BM : 0;
+      const int v = e < E ? max(0, group_off<KG>(offsets, Mg, e + 1) - group_off<KG>(offsets, Mg, e) + BM - 1) / BM
+                          : 0;
       int incl = v;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
@@ -813,7 +818,7 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uin
 #define GG_LAUNCH(KT, OB)                                                                    \
   g5::grouped_gemm_kernel<KT, OB, false, false><<<(unsigned)grid, g5::kThreads, 0, s>>>(      \
       a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales, (int)N, \
-      (int)K, c, nullptr, nullptr, 0, nullptr, 0)
+      (int)K, c, nullptr, nullptr, 0, nullptr, (int)R_cap)
   const bool kt = w_layout == NVFP4_W_KTILED, ob = c_dtype == NVFP4_OUT_BF16;
   if (kt && !ob) GG_LAUNCH(true, false);
   else if (kt) GG_LAUNCH(true, true);
@@ -872,7 +877,7 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm_swiglu(
   }
   g5::grouped_gemm_kernel<true, false, true, false><<<(unsigned)grid, g5::kThreads, 0, s>>>(
       a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales,
-      (int)(2 * I), (int)K, h, w_rows, gu, (int)I, nullptr, 0);
+      (int)(2 * I), (int)K, h, w_rows, gu, (int)I, nullptr, (int)R_cap);
   return launch_status();
 }
 

@@ -657,15 +657,19 @@ __global__ __launch_bounds__(kQrWaves * 64) void quantize_permute_rows_kernel(
 // FP32, then the row quantiser; the amax is taken on the values just made.
 template <int NCH>
 __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
-    const float* __restrict__ gu, int I, const int32_t* __restrict__ offsets, int E,
+    const float* __restrict__ gu, int64_t R_cap, int I, const int32_t* __restrict__ offsets, int E,
     const float* __restrict__ topk_w, const int32_t* __restrict__ row_to_tk,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales, float* __restrict__ rscales,
     float* __restrict__ h_out) {
   const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (r >= offsets[E]) return;
+  if (r >= offsets[E] || r >= R_cap) return;
   const int lane = lane_id();
   const float* grow = gu + r * (int64_t)(2 * I);
-  const float w = topk_w ? topk_w[row_to_tk[r]] : 1.0f;
+  float w = 1.0f;
+  if (topk_w) {   // the router weight of the row's (token, slot); a bad map entry gives 0
+    const int32_t i = row_to_tk[r];
+    w = (i >= 0 && i < R_cap) ? topk_w[i] : 0.0f;
+  }
   // SwiGLU of one element: float64, in the order of the definition, rounded once
   auto swiglu = [&](float gf, float uf) __attribute__((always_inline)) -> float {
     const double g = gf;
@@ -807,10 +811,12 @@ __global__ __launch_bounds__(256) void quantize_tokens_kernel(
   const int c = (int)blockIdx.x * 256 + 8 * cg;                  // first of the thread's 8 columns
   const int r0 = offsets[e], n = offsets[e + 1] - r0;
   const int kb0 = kofs[e], nblk = (kofs[e + 1] - kb0) * 4;      // blocks of 16 tokens in the slab
-  if ((int64_t)(kofs[e + 1]) * 64 > Kp) return;                  // slab outside the buffer: skipped
+  if (kb0 < 0 || kofs[e + 1] < kb0 || (int64_t)(kofs[e + 1]) * 64 > Kp) return;   // slab outside the buffer: skipped
   auto load8 = [&](int r, float (&v)[8]) __attribute__((always_inline)) {
     int64_t xr = r0 + r;
-    if (row_to_tk) xr = row_to_tk[xr] / k;
+    // token-order input: the routing map has x_rows * k entries; a bad offset or
+    // map entry reads a wrong row, never one outside x
+    if (row_to_tk) xr = row_to_tk[min(max(xr, (int64_t)0), x_rows * k - 1)] / k;
     xr = xr < 0 ? 0 : (xr >= x_rows ? x_rows - 1 : xr);
     if constexpr (F32IN) {
       const float* p = static_cast<const float*>(x) + xr * C + c;
@@ -1201,7 +1207,7 @@ NVFP4MOE_API int swiglu_quantize(const float* gu, int64_t R_cap, int64_t I,
     return NVFP4_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)((R_cap + kRowsPerBlock - 1) / kRowsPerBlock));
-  NVFP4_DISPATCH_NCH(I, swiglu_quantize_kernel, grid, s, gu, (int)I, expert_offsets, E, topk_w,
+  NVFP4_DISPATCH_NCH(I, swiglu_quantize_kernel, grid, s, gu, R_cap, (int)I, expert_offsets, E, topk_w,
                      row_to_tk, codes, bscales, rscales, h_out);
   return launch_status();
 }
