@@ -225,8 +225,9 @@ NVFP4MOE_API int nvfp4_quantize_permute_noalloc(const uint16_t* x, int64_t T, in
  * E = 1 with expert_offsets = {0, M} is a dense GEMM of M rows.  The list of
  * (expert, row block, column block) tiles is derived on the device from
  * expert_offsets by every workgroup (no tile list argument).
- * expert_offsets must be non-decreasing with expert_offsets[E] <= R_cap (as
- * nvfp4_quantize_permute writes them).
+ * expert_offsets are read as nvfp4_quantize_permute writes them (non-decreasing,
+ * expert_offsets[E] <= R_cap); the kernel clamps each into [0, R_cap], so other
+ * values give wrong rows but no access outside the buffers.
  * Requires K % 64 == 0, N % 16 == 0, 16 <= N <= 2^20, K <= 65536, all pointers
  * 16-byte aligned.  Unknown w_layout or c_dtype: NVFP4_ERR_ARG.
  */
@@ -324,7 +325,9 @@ NVFP4MOE_API int nvfp4_quantize_rows_f32(const float* x, int64_t rows, int64_t K
  *   c          [E][M][N] of c_dtype: NVFP4_OUT_F32 (float) or NVFP4_OUT_BF16 (bf16 bits,
  *              each FP32 result rounded to nearest even)
  * Requires N % 16 == 0, 16 <= N <= 2^20, Kp % 64 == 0, M * Kp / 2 and
- * N * Kp / 2 below 2^32, kofs[E] <= Kp / 64.
+ * N * Kp / 2 below 2^32.  kofs as nvfp4moe_token_blocks writes it (kofs[E] <=
+ * Kp / 64); each expert's range is clamped into [0, Kp / 64) with at least one
+ * K-step, so other values give wrong results but no access outside the buffers.
  */
 #define NVFP4_IN_BF16 0
 #define NVFP4_IN_F32 1
@@ -346,7 +349,8 @@ NVFP4MOE_API int nvfp4_grouped_gemm_wgrad(const uint8_t* a_codes, const uint8_t*
  * on the fly, then NVFP4 quantisation of each routed row (for the down GEMM).
  *   gu        float [R_cap][2I]: gate = columns [0, I), up = columns [I, 2I)
  *   topk_w    float [T*k] router weight of (t, slot) (NULL: weight 1)
- *   row_to_tk int32 [R_cap] from nvfp4_quantize_permute (needed if topk_w)
+ *   row_to_tk int32 [R_cap] from nvfp4_quantize_permute (needed if topk_w; an entry
+ *             outside [0, R_cap) gives that row the router weight 0)
  *   h = float32( ((g / (1 + exp(-g))) * u) * w ), evaluated in FP64
  *   codes [R_cap][I/2], bscales [R_cap][I/16], rscales [R_cap]: NVFP4 of h
  *   h_out     float [R_cap][I] (NULL: not written)
@@ -363,8 +367,9 @@ NVFP4MOE_API int swiglu_quantize(const float* gu, int64_t R_cap, int64_t I,
  *   acc = w_0 * d[row(t,0)];  acc = acc + w_s * d[row(t,s)]  (s = 1..k-1)
  * in FP32, slot order, no fused multiply-add; y[t] = bf16(acc) (nearest even).
  * w_s = 1 when topk_w is NULL (the router weight already applied in
- * swiglu_quantize).  Pairs with tk_to_row = -1 are skipped.
- *   d float [R_cap][H]; tk_to_row int32 [T*k]; y bf16 bits [T][H]
+ * swiglu_quantize).  Pairs with tk_to_row = -1 are skipped, and so are entries at
+ * or beyond T*k (d holds R_cap = T*k rows).
+ *   d float [T*k][H]; tk_to_row int32 [T*k]; y bf16 bits [T][H]
  * Requires H % 8 == 0, 1 <= k <= NVFP4MOE_MAX_TOPK.
  */
 NVFP4MOE_API int unpermute_combine(const float* d, int64_t T, int32_t k, int64_t H,
@@ -373,8 +378,9 @@ NVFP4MOE_API int unpermute_combine(const float* d, int64_t T, int32_t k, int64_t
 
 /*
  * permute_gather_bf16 - copy token rows to their routed rows (backward input):
- *   out[r] = x[row_to_tk[r] / k]  for r < expert_offsets[E]
- *   x bf16 bits [T][H]; out bf16 bits [R_cap][H].  Requires H % 8 == 0.
+ *   out[r] = x[row_to_tk[r] / k]  for r < expert_offsets[E] (and r < T*k)
+ *   x bf16 bits [T][H]; out bf16 bits [T*k][H]; a token index outside [0, T) is
+ *   clamped into it.  Requires H % 8 == 0.
  */
 NVFP4MOE_API int permute_gather_bf16(const uint16_t* x, int64_t T, int64_t H, int32_t k,
                                      const int32_t* expert_offsets, int32_t E,
@@ -424,6 +430,7 @@ NVFP4MOE_API int bf16_grouped_gemm_gather(const uint16_t* a, int64_t T, const in
  *   gu float [R_cap][2I] (forward gate_up output); dh float [R_cap][I]
  *   topk_w / row_to_tk as in swiglu_quantize (NULL topk_w: w = 1)
  *   dgu bf16 bits [R_cap][2I]: [0, I) = dg, [I, 2I) = du
+ * A row_to_tk entry outside [0, R_cap) gives that row the router weight 0.
  * Requires I % 8 == 0.
  */
 NVFP4MOE_API int swiglu_backward(const float* gu, const float* dh, int64_t R_cap, int64_t I,
