@@ -13,10 +13,12 @@
 // bytes in flight and reads every byte from L2 as few times as it can:
 //   * one 512-thread workgroup per CU, tiles of up to 320 rows x 256 columns
 //     (8 wavefronts of up to 160 x 64; the two wavefront rows take alternate
-//     16-row groups), K-step 32.  The tile height (320, 256, 192, 128 or 64)
-//     is picked per launch from the routing: an expert of up to 320 rows then
-//     streams each weight slab once, while a skewed routing gets shorter tiles
-//     that spread its large experts over more workgroups;
+//     16-row groups), K-step 32.  The tile height (320, 256, 192, 160, 128 or
+//     64) is picked per launch from the routing: an expert of up to 320 rows
+//     then streams each weight slab once, while a skewed routing gets shorter
+//     tiles that spread its large experts over more workgroups; an expert's
+//     rows are split evenly over its tiles (in 16-row groups), so that its
+//     tiles cost about the same;
 //   * the MFMA loop is compiled once per count of 16-row groups a wavefront
 //     holds, so a partial tile runs straight-line code with every fragment
 //     read issued before its MFMAs;
@@ -46,8 +48,8 @@ namespace gb {
 // (kHeights) is chosen per launch from the routing.
 constexpr int BM = 320, WM = BM / 2, FM = WM / 16;
 constexpr int BN = 256, BK = 32;
-constexpr int kNumHeights = 5;
-constexpr int kHeights[kNumHeights] = {320, 256, 192, 128, 64};
+constexpr int kNumHeights = 6;
+constexpr int kHeights[kNumHeights] = {320, 256, 192, 160, 128, 64};
 constexpr int kTileCost = 96;                 // rows' worth of per-tile cost (see the kernel)
 constexpr int kWaves = 8, kThreads = kWaves * 64;
 constexpr int kLdsStages = 147456;            // LDS for the stage ring (144 KiB)
@@ -76,9 +78,16 @@ struct __align__(16) Smem {
   int bm;
 };
 
-// physical 16-byte chunk of logical chunk c (0..3) of row r: rows r..r+15 of
-// one fragment read land in 16 distinct 16-byte bank groups
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+// physical 16-byte chunk of logical chunk c (0..3) of row r.  A 16-byte LDS
+// read (ds_read_b128) on gfx950 is served in four passes of 16 lanes; a pass
+// takes, from one half of the wavefront (lanes 0-31 or 32-63), the four lane
+// quads whose quad index (lane / 4) mod 8 has the same bit parity, and is
+// conflict-free when its 16 reads fall on the 16 distinct 16-byte bank groups
+// of a 256-byte window (measured with SQ_LDS_BANK_CONFLICT on single-pattern
+// kernels).  A fragment read gives lane (l, g) row r0 + l (l < 16), chunk g:
+// with the XOR below each pass covers rows 4i..4i+3 of two row quads whose
+// XOR terms differ, i.e. 16 distinct (row mod 4, chunk) pairs.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 2) & 2); }
 
 // [K][N] weight tile: physical 16-byte chunk p of row k holds logical chunk
 // p ^ wswz(k).  A transposing read covers rows k0..k0+3 in each group of 16
@@ -142,8 +151,14 @@ __device__ __forceinline__ Tile tile_at(int L, int n_tiles, int bm, const int* t
   }
   Tile t;
   t.e = __builtin_amdgcn_readfirstlane(lo);
-  t.m0 = __builtin_amdgcn_readfirstlane(off_at(offsets, Rc, t.e) + (tm - tile_start[t.e]) * bm);
-  t.rows = __builtin_amdgcn_readfirstlane(min(bm, off_at(offsets, Rc, t.e + 1) - t.m0));
+  // the expert's rows split evenly over its nt = ceil(rows / bm) m-tiles, in
+  // 16-row groups: per <= bm (bm is a multiple of 16), and (nt - 1) * per <
+  // rows, so no tile is empty or taller than bm
+  const int o0 = off_at(offsets, Rc, t.e), o1 = off_at(offsets, Rc, t.e + 1);
+  const int nt = tile_start[t.e + 1] - tile_start[t.e];
+  const int per = ((o1 - o0 + nt - 1) / nt + 15) & ~15;
+  t.m0 = __builtin_amdgcn_readfirstlane(o0 + (tm - tile_start[t.e]) * per);
+  t.rows = __builtin_amdgcn_readfirstlane(max(0, min(per, o1 - t.m0)));
   t.n0 = tn * BN;
   return t;
 }
