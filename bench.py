@@ -335,7 +335,8 @@ def main():
     step()
     torch.cuda.synchronize()
 
-    result["practical_ceiling"] = practical_ceiling(gu_tf, per_op["quantize_permute"]["GBps"])
+    result["practical_ceiling"] = practical_ceiling(gu_tf, per_op["quantize_permute"]["GBps"],
+                                                    op_bytes["quantize_permute"])
     if not args.no_comparisons:
         result["comparisons"] = comparisons(
             dict(x=x, dy=dy, ids=ids, E=E, k=k, I=I, H=H, perm=perm, wgu=wgu, wd=wd, dgu=dgu, dh=dh, ws=ws,
@@ -587,10 +588,12 @@ def weight_gradients(t):
     return res
 
 
-def practical_ceiling(gate_up_tflops, qp_gbps):
+def practical_ceiling(gate_up_tflops, qp_gbps, qp_bytes):
     """Rates the device sustains, measured after the timed steps (outside them):
-    FP16 MFMA issue with no memory traffic (the library's MFMA-only kernel) and a
-    512 MiB device-to-device copy; the headline kernels as fractions of these."""
+    FP16 MFMA issue with no memory traffic (the library's MFMA-only kernel), a
+    512 MiB device-to-device copy, and a copy that moves the quantize-permute's
+    algorithmic bytes (half read, half written) timed like it (cold, HIP events
+    around one launch); the headline kernels as fractions of these."""
     import torch
     import precision_moe_gemm_amd as pmg
     st, en = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -615,11 +618,22 @@ def practical_ceiling(gate_up_tflops, qp_gbps):
     en.record()
     torch.cuda.synchronize()
     copy_gbs = 10 * 2 * n * 4 / (st.elapsed_time(en) * 1e-3) / 1e9
+    del a, b
+    m = int(qp_bytes) // 8                  # floats copied: 4 m bytes read + 4 m written
+    a2 = torch.ones(m, dtype=torch.float32, device="cuda")
+    b2 = torch.empty_like(a2)
+    small_us = time_cold(lambda: b2.copy_(a2), 20)
+    small_gbs = 8 * m / (small_us * 1e-6) / 1e9
     return {"mfma_f16_tflops": round(mfma_tf, 1), "copy_gbps": round(copy_gbs, 1),
             "gate_up_frac_of_mfma": round(gate_up_tflops / mfma_tf, 4),
             "quantize_permute_frac_of_copy": round(qp_gbps / copy_gbs, 4),
+            "copy_of_quantize_permute_bytes": {"bytes": 8 * m, "us": round(small_us, 2),
+                                               "GBps": round(small_gbs, 1),
+                                               "frac_hbm_peak": round(small_gbs / 8000.0, 4)},
+            "quantize_permute_frac_of_same_bytes_copy": round(qp_gbps / small_gbs, 4),
             "how": "MFMA: 256 workgroups x 8 wavefronts of back-to-back 32x32x16 f16 MFMAs on registers; "
-                   "copy: 512 MiB device-to-device, read + write bytes"}
+                   "copy: 512 MiB device-to-device, read + write bytes; copy of the quantize-permute's "
+                   "bytes: one device-to-device copy launch after a 512 MiB cache-evicting write"}
 
 
 def cpu_baseline(x_bits, ids, wgu_bits, S, budget_s):

@@ -357,41 +357,55 @@ __global__ __launch_bounds__(256) void quantize_rows_tiled_kernel(
 
 // Route + permute + quantise in two launches.
 //
-// The rank pass: workgroup c (16 wavefronts) takes chunk c of 4096 routing
-// entries.  Each wavefront ranks its 256 entries in 4 passes of 64
-// consecutive ones by ballot matching on the expert id, keeping a running
-// count per expert in LDS; an exclusive scan of those counts over the
-// wavefronts gives every entry its stable rank among the chunk's entries of
-// its expert (entry order: token, then slot).  The ranks go to the workspace
-// and the chunk's counts per expert to the table, cnt[c][e].  Workgroups are
-// independent; the launch boundary publishes the results.
+// The rank pass: workgroup c (16 wavefronts) takes chunk c of 2^L routing
+// entries (L = 11 or 12, chosen per launch by plan_chunk_log).  Each
+// wavefront ranks its 2^L / 16 entries in passes of 64 consecutive ones by
+// ballot matching on the expert id, keeping a running count per expert in
+// LDS; an exclusive scan of those counts over the wavefronts gives every entry
+// its stable rank among the chunk's entries of its expert (entry order: token,
+// then slot).  The ranks go to the workspace and the chunk's counts per expert
+// to the table, cnt[c][e].  Workgroups are independent; the launch boundary
+// publishes the results.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;
-constexpr int kPlanChunkLog = 12;        // 4096 routing entries per chunk
-constexpr int kPlanChunk = 1 << kPlanChunkLog;
+constexpr int kPlanChunkLogMin = 11;     // 2048 routing entries per chunk: two passes per wavefront
+constexpr int kPlanChunkLogMax = 12;     // 4096: four passes
 constexpr int kCountTable = 4096;        // ints of (chunk, expert) counts the main pass scans
 
-inline int plan_chunks(int64_t n) { return n > 0 ? (int)((n + kPlanChunk - 1) >> kPlanChunkLog) : 1; }
+inline int plan_chunks(int64_t n, int lg) { return n > 0 ? (int)((n + (1ll << lg) - 1) >> lg) : 1; }
+
+// The smallest chunk whose count table still fits the main pass (more
+// workgroups share the ranking of a short list), else the largest.  (At 4096
+// tokens x 8 of 128 experts, chunks of 2048 entries measured best: 1024 gives
+// each main-pass workgroup a 4096-int table to scan, 4096 leaves the rank pass
+// on 8 workgroups.)
+inline int plan_chunk_log(int64_t n, int E) {
+  for (int lg = kPlanChunkLogMin; lg < kPlanChunkLogMax; ++lg)
+    if ((int64_t)plan_chunks(n, lg) * E <= kCountTable) return lg;
+  return kPlanChunkLogMax;
+}
 
 __global__ __launch_bounds__(kPlanThreads) void route_rank_kernel(
-    const int32_t* __restrict__ ids, int n, int E, int32_t* __restrict__ cnt_out,
+    const int32_t* __restrict__ ids, int n, int E, int chunk_log, int32_t* __restrict__ cnt_out,
     int32_t* __restrict__ rank_out, int32_t* __restrict__ dev_err) {
   __shared__ int32_t wcnt[kPlanWaves][NVFP4MOE_MAX_EXPERTS];   // per wavefront, then its exclusive prefix
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int base = (blockIdx.x << kPlanChunkLog) + wave * 256;   // this wavefront's 256 entries
+  const int passes = (1 << chunk_log) / kPlanThreads;           // passes of 64 per wavefront (<= 4)
+  const int base = (blockIdx.x << chunk_log) + wave * 64 * passes;   // this wavefront's entries
   int ev[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = base + 64 * u + lane;
-    ev[u] = i < n ? ids[i] : -1;
+    ev[u] = (u < passes && i < n) ? ids[i] : -1;
   }
   for (int e = lane; e < E; e += kWave) wcnt[wave][e] = 0;   // each wavefront clears its own row
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  int lr[4];
+  int lr[4] = {-1, -1, -1, -1};
   bool bad = false;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
+    if (u >= passes) break;
     const int i = base + 64 * u + lane;
     const int e = ev[u];
     const bool valid = i < n && e >= 0 && e < E;
@@ -427,26 +441,35 @@ __global__ __launch_bounds__(kPlanThreads) void route_rank_kernel(
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = base + 64 * u + lane;
-    if (i < n) rank_out[i] = lr[u] >= 0 ? wcnt[wave][ev[u]] + lr[u] : -1;
+    if (u < passes && i < n) rank_out[i] = lr[u] >= 0 ? wcnt[wave][ev[u]] + lr[u] : -1;
   }
 }
 
 // The main pass.  Workgroup w (8 wavefronts) owns tokens [8w, 8w + 8), one
-// per wavefront.  Every load it needs is issued at the start: the token's
-// activations, its k expert ids and ranks, and the count table.  The token is
-// quantised first (its codes do not depend on the routing); the workgroup
-// then forms, from the table, the expert offsets and the first row of each
-// expert in the chunk(s) its entries fall in, and an entry's row is that
-// first row plus its rank.  Each token is written to its k rows.  Workgroup 0
-// also writes the expert offsets.
+// per wavefront.  Every load it needs is issued at the start: the count table
+// and the token's k expert ids and ranks first, then the token's activations.
+// While the activations are in flight the workgroup forms, from the table,
+// the expert offsets and the first row of each expert in the chunk(s) its
+// entries fall in; an entry's row is that first row plus its rank.  Then the
+// token is quantised and written to its k rows.  Workgroup 0 also writes the
+// expert offsets.  Every load is issued unconditionally (indices clamped into
+// the arrays) and the workgroup barriers order LDS only, so that waiting for
+// the routing loads leaves the activations in flight.
 constexpr int kQpWaves = 8;
 constexpr int kQpThreads = kQpWaves * 64;
 constexpr int kQpExp = NVFP4MOE_MAX_EXPERTS / kQpThreads;   // experts per thread (2)
 
+// workgroup barrier for LDS only: global loads in flight are not waited for
+__device__ __forceinline__ void lds_only_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int NCH, int BPL>
 __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
     const uint16_t* __restrict__ x, int64_t T, int K, const int32_t* __restrict__ ids, int k, int E,
-    const int32_t* __restrict__ cnt, const int32_t* __restrict__ rank, int nchunks,
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ rank, int nchunks, int chunk_log,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales, float* __restrict__ rscales,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_to_tk, int32_t* __restrict__ tk_to_row) {
   __shared__ int32_t sbase[2][NVFP4MOE_MAX_EXPERTS];   // first row of expert e in chunk c0, c0 + 1
@@ -455,45 +478,31 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
   const int lane = lane_id(), wave = threadIdx.x >> 6, tid = threadIdx.x;
   const int64_t t = (int64_t)blockIdx.x * kQpWaves + wave;
   const int e0 = (int)((int64_t)blockIdx.x * kQpWaves * k);       // first entry of the group
-  const int c0 = e0 >> kPlanChunkLog;                              // its chunk
+  const int c0 = e0 >> chunk_log;                                  // its chunk
+  const int n = (int)(T * k);                                      // routing entries (T >= 1)
+  const int ntab = nchunks * E;
 
-  // every load first: activations, this token's entries, the count table
+  // every load first: the count table and this token's entries, then its activations
+  int tv[kCountTable / kQpThreads];             // the table, 8 independent loads per thread
+#pragma unroll
+  for (int u = 0; u < kCountTable / kQpThreads; ++u) tv[u] = cnt[min(u * kQpThreads + tid, ntab - 1)];
+  const int my_i = (int)(t * k) + lane;
+  const bool mine = t < T && lane < k;          // lane < k holds entry my_i of this token
+  const int my_e = ids[min(my_i, n - 1)];
+  const int my_r = rank[min(my_i, n - 1)];
   constexpr bool kC = BPL > 0;                 // contiguous-lane rows
   uint4 raw[kC ? 2 * BPL : NCH];
-  if (t < T) {
-    if constexpr (kC) load_bf16_c<BPL>(x + t * (int64_t)K, raw);
-    else load_bf16_raw<NCH>(x + t * (int64_t)K, K, raw);
-  }
-  int my_e = -1, my_r = -1;
-  const int my_i = (int)(t * k) + lane;
-  if (t < T && lane < k) {
-    my_e = ids[my_i];
-    my_r = rank[my_i];
-  }
-  int tv[kCountTable / kQpThreads];             // the table, 8 independent loads per thread
+  const int64_t tl = min(t, T - 1);
+  if constexpr (kC) load_bf16_c<BPL>(x + tl * (int64_t)K, raw);
+  else load_bf16_raw<NCH>(x + tl * (int64_t)K, K, raw);
+
+  // the table: per expert the total and the entries in chunks before c0, c0 + 1
 #pragma unroll
   for (int u = 0; u < kCountTable / kQpThreads; ++u) {
     const int i = u * kQpThreads + tid;
-    tv[u] = i < nchunks * E ? cnt[i] : 0;
+    tab[i] = i < ntab ? tv[u] : 0;
   }
-  // the token's codes
-  RowCodes<NCH> o;
-  RowCodesC<kC ? BPL : 1> oc;
-  uint32_t sw[(NCH + 7) / 8];
-  if (t < T) {
-    if constexpr (kC) {
-      quantize_lane_row_c<BPL>(raw, oc);
-    } else {
-      float v[NCH][8];
-      unpack_bf16<NCH>(raw, v);
-      quantize_lane_row<NCH>(v, o);
-      pack_scales<NCH>(o, sw);
-    }
-  }
-  // the table: per expert the total and the entries in chunks before c0, c0 + 1
-#pragma unroll
-  for (int u = 0; u < kCountTable / kQpThreads; ++u) tab[u * kQpThreads + tid] = tv[u];
-  __syncthreads();
+  lds_only_barrier();
   int tot[kQpExp], b0[kQpExp], b1[kQpExp];
 #pragma unroll
   for (int u = 0; u < kQpExp; ++u) { tot[u] = 0; b0[u] = 0; b1[u] = 0; }
@@ -508,20 +517,20 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
     }
   }
   // expert offsets: exclusive scan of the totals over experts
-  int mine = 0;
+  int mine_tot = 0;
 #pragma unroll
-  for (int u = 0; u < kQpExp; ++u) mine += tot[u];
-  int incl = mine;
+  for (int u = 0; u < kQpExp; ++u) mine_tot += tot[u];
+  int incl = mine_tot;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
     const int y = __shfl_up(incl, off, kWave);
     if (lane >= off) incl += y;
   }
   if (lane == kWave - 1) wsum[wave] = incl;
-  __syncthreads();
+  lds_only_barrier();
   int before = 0;
   for (int w = 0; w < wave; ++w) before += wsum[w];
-  int off_e = before + incl - mine;   // offset of expert kQpExp * tid
+  int off_e = before + incl - mine_tot;   // offset of expert kQpExp * tid
 #pragma unroll
   for (int u = 0; u < kQpExp; ++u) {
     const int e = kQpExp * tid + u;
@@ -533,13 +542,26 @@ __global__ __launch_bounds__(kQpThreads) void quantize_permute_kernel(
     off_e += tot[u];
   }
   if (blockIdx.x == 0 && tid == kQpThreads - 1) offsets[E] = before + incl;
-  __syncthreads();
+  lds_only_barrier();
   if (t >= T) return;
+  // the rows of this token's entries (a rank >= 0 marks a valid expert id)
   int row = -1;
-  if (lane < k) {
-    if (my_r >= 0) row = sbase[(my_i >> kPlanChunkLog) - c0][my_e] + my_r;
+  if (mine) {
+    if (my_r >= 0) row = sbase[(my_i >> chunk_log) - c0][my_e] + my_r;
     tk_to_row[my_i] = row;
     if (row >= 0) row_to_tk[row] = my_i;
+  }
+  // the token's codes (its activations have landed meanwhile)
+  RowCodes<NCH> o;
+  RowCodesC<kC ? BPL : 1> oc;
+  uint32_t sw[(NCH + 7) / 8];
+  if constexpr (kC) {
+    quantize_lane_row_c<BPL>(raw, oc);
+  } else {
+    float v[NCH][8];
+    unpack_bf16<NCH>(raw, v);
+    quantize_lane_row<NCH>(v, o);
+    pack_scales<NCH>(o, sw);
   }
   for (int slot = 0; slot < k; ++slot) {
     const int r = __shfl(row, slot, kWave);
@@ -615,9 +637,9 @@ constexpr int kQrWaves = 4;
 template <int NCH, int BPL>
 __global__ __launch_bounds__(kQrWaves * 64) void quantize_permute_rows_kernel(
     const uint16_t* __restrict__ x, int64_t T, int K, const int32_t* __restrict__ ids, int k, int E,
-    const int32_t* __restrict__ base, const int32_t* __restrict__ rank, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ bscales, float* __restrict__ rscales, int32_t* __restrict__ row_to_tk,
-    int32_t* __restrict__ tk_to_row) {
+    const int32_t* __restrict__ base, const int32_t* __restrict__ rank, int chunk_log,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales, float* __restrict__ rscales,
+    int32_t* __restrict__ row_to_tk, int32_t* __restrict__ tk_to_row) {
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * kQrWaves + wave;
   if (t >= T) return;
@@ -629,7 +651,7 @@ __global__ __launch_bounds__(kQrWaves * 64) void quantize_permute_rows_kernel(
   if (lane < k) {
     const int i = (int)(t * k) + lane;
     const int e = ids[i], r = rank[i];
-    if (r >= 0) row = base[(int64_t)(i >> kPlanChunkLog) * E + e] + r;
+    if (r >= 0) row = base[(int64_t)(i >> chunk_log) * E + e] + r;
     tk_to_row[i] = row;
     if (row >= 0) row_to_tk[row] = i;
   }
@@ -947,7 +969,7 @@ NVFP4MOE_API size_t nvfp4moe_permute_workspace_size(int64_t T, int32_t k, int32_
   if (T < 0 || k <= 0 || E <= 0) return 0;
   // the (chunk, expert) count table and a rank per routing entry
   const int64_t n = T * (int64_t)k;
-  const size_t bytes = ((size_t)plan_chunks(n) * (size_t)E + (size_t)n) * sizeof(int32_t);
+  const size_t bytes = ((size_t)plan_chunks(n, plan_chunk_log(n, E)) * (size_t)E + (size_t)n) * sizeof(int32_t);
   return (bytes + 255) & ~(size_t)255;
 }
 
@@ -1081,19 +1103,21 @@ static int quantize_permute_impl(const uint16_t* x, int64_t T, int64_t H, const 
   if (workspace_bytes < nvfp4moe_permute_workspace_size(T, k, E)) return NVFP4_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t n = T * (int64_t)k;
-  const int pchunks = plan_chunks(n);
+  const int chunk_log = plan_chunk_log(n, E);
+  const int pchunks = plan_chunks(n, chunk_log);
   int32_t* table = static_cast<int32_t*>(workspace);        // [pchunks][E]
   int32_t* rank = table + (int64_t)pchunks * E;              // [n]
   // rank every entry within its chunk and expert, and count per (chunk, expert)
-  route_rank_kernel<<<pchunks, kPlanThreads, 0, s>>>(topk_ids, (int)n, E, table, rank, dev_err);
+  route_rank_kernel<<<pchunks, kPlanThreads, 0, s>>>(topk_ids, (int)n, E, chunk_log, table, rank,
+                                                     dev_err);
   if (T > 0 && (int64_t)pchunks * E <= kCountTable && H <= 4096) {
     // offsets + first rows from the table in every workgroup, then rows +
     // quantise + scatter
     const unsigned grid = (unsigned)((T + kQpWaves - 1) / kQpWaves);
 #define QP_LAUNCH(C, B)                                                                          \
     quantize_permute_kernel<C, B><<<grid, kQpThreads, 0, s>>>(x, T, (int)H, topk_ids, (int)k,     \
-        (int)E, table, rank, pchunks, codes, bscales, rscales, expert_offsets, row_to_tk,         \
-        tk_to_row)
+        (int)E, table, rank, pchunks, chunk_log, codes, bscales, rscales, expert_offsets,         \
+        row_to_tk, tk_to_row)
     // rows of 1024, 2048 or 4096 elements: contiguous lanes; other lengths: strided lanes
     if (H == 1024) QP_LAUNCH(2, 1);
     else if (H == 2048) QP_LAUNCH(4, 2);
@@ -1117,7 +1141,7 @@ static int quantize_permute_impl(const uint16_t* x, int64_t T, int64_t H, const 
     const unsigned grid = (unsigned)((T + kQrWaves - 1) / kQrWaves);
 #define QR_LAUNCH(C, B)                                                                          \
     quantize_permute_rows_kernel<C, B><<<grid, kQrWaves * 64, 0, s>>>(x, T, (int)H, topk_ids,     \
-        (int)k, (int)E, table, rank, codes, bscales, rscales, row_to_tk, tk_to_row)
+        (int)k, (int)E, table, rank, chunk_log, codes, bscales, rscales, row_to_tk, tk_to_row)
     if (H == 1024) QR_LAUNCH(2, 1);
     else if (H == 2048) QR_LAUNCH(4, 2);
     else if (H == 4096) QR_LAUNCH(8, 4);
@@ -1141,9 +1165,15 @@ static int quantize_permute_impl(const uint16_t* x, int64_t T, int64_t H, const 
 // device holds its own copy while the process lives).  Host code never passes
 // the array's name to a kernel: it stands for the host-side shadow, so the
 // device address is looked up once per device and kept in scratch_ptr.
+// (A chunk shorter than the largest is only chosen when its table fits
+// kCountTable words, which the largest chunk's table bound covers.)
 constexpr int64_t kNoAllocWords =
-    (int64_t)((NVFP4MOE_NOALLOC_MAX_ENTRIES + kPlanChunk - 1) >> kPlanChunkLog) * NVFP4MOE_MAX_EXPERTS +
+    (int64_t)((NVFP4MOE_NOALLOC_MAX_ENTRIES + (1 << kPlanChunkLogMax) - 1) >> kPlanChunkLogMax) *
+        NVFP4MOE_MAX_EXPERTS +
     NVFP4MOE_NOALLOC_MAX_ENTRIES;
+static_assert((1 << kPlanChunkLogMax) / kPlanThreads <= 4, "at most four passes of 64 per wavefront");
+static_assert((int64_t)((NVFP4MOE_NOALLOC_MAX_ENTRIES + (1 << kPlanChunkLogMax) - 1) >> kPlanChunkLogMax) *
+                  NVFP4MOE_MAX_EXPERTS >= kCountTable, "scratch holds a count table of kCountTable words");
 static __device__ __align__(256) int32_t scratch[kNoAllocWords];
 
 constexpr int kMaxDevices = 64;

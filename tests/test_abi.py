@@ -43,7 +43,7 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_size(lib):
-    # a (chunk of 4096 entries, expert) count table and one rank per routing entry
+    # a (chunk of 2048 or 4096 entries, expert) count table and one rank per routing entry
     assert lib.nvfp4moe_permute_workspace_size(4096, 8, 128) >= (8 * 128 + 32768) * 4
     assert lib.nvfp4moe_permute_workspace_size(0, 8, 128) >= 128 * 4
     assert lib.nvfp4moe_permute_workspace_size(-1, 8, 128) == 0

@@ -135,9 +135,11 @@ def test_quantize_permute_full_config():
                                           (1000, 128, 8, "zipf"), (777, 16, 3, "uniform"),
                                           (2049, 64, 8, "softmax"), (300, 1, 1, "uniform"),
                                           (128, 1024, 32, "uniform"),   # E > 512
-                                          (2000, 32, 3, "zipf"),        # groups of 24 entries straddle 4096-entry chunks
-                                          (1700, 64, 5, "softmax"),     # ditto, 3 chunks
-                                          (600, 1024, 8, "uniform"),    # 2 chunks x 1024 experts in the count table
+                                          (2000, 32, 3, "zipf"),        # groups of 24 entries straddle 2048-entry chunks
+                                          (1700, 64, 5, "softmax"),     # ditto, 5 chunks
+                                          (600, 1024, 8, "uniform"),    # 3 chunks x 1024 experts in the count table
+                                          (10000, 128, 8, "zipf"),      # 20 chunks of 4096 (40 of 2048 would not fit the table)
+                                          (3000, 512, 7, "zipf"),       # 6 chunks of 4096 x 512 experts, groups of 56 straddle them
                                           (40000, 128, 8, "zipf"),      # 79 chunks: first rows by one workgroup, 8 threads per expert
                                           (60000, 100, 6, "zipf"),      # 88 chunks, 10 scan threads per expert (1000 of 1024)
                                           (3000, 1024, 32, "uniform")]) # 24 chunks x 1024 experts: one scan thread per expert
