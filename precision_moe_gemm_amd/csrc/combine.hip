@@ -60,6 +60,68 @@ __global__ __launch_bounds__(256) void unpermute_combine_kernel(
   }
 }
 
+// The same sum for rows of H = 256 NC elements, slot by slot: lane l holds
+// columns 4l + 256c (c < NC) of the token's sum, and each routed row is read
+// whole (NC loads of 1 KiB per wavefront, one after another) before the next
+// slot's, so a row's DRAM pages are read in one go.  The loads of G = 16 / NC
+// slots are issued before the first of them is added (16 loads of 16 bytes per
+// lane in flight); the sum runs in slot order with the same products and sums
+// as unpermute_combine_kernel, so the results are identical.
+template <int NC>
+__global__ __launch_bounds__(256) void unpermute_combine_rows_kernel(
+    const float* __restrict__ d, int64_t T, int k, const int32_t* __restrict__ tk_to_row,
+    const float* __restrict__ topk_w, uint16_t* __restrict__ y) {
+  constexpr int H = 256 * NC;
+  constexpr int G = NC >= 16 ? 1 : 16 / NC;      // slots per group
+  const int64_t t = (int64_t)blockIdx.x * kRows + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = lane_id();
+  const int my_row = lane < k ? tk_to_row[t * k + lane] : -1;
+  const float my_w = (lane < k && topk_w) ? topk_w[t * k + lane] : 1.0f;
+  float4 acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  bool started = false;
+  for (int s0 = 0; s0 < k; s0 += G) {
+    float4 v[G][NC];
+    float wv[G];
+    bool ok[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int sl = s0 + u;                         // < 48: a lane index
+      const int row = __shfl(my_row, sl, kWave);
+      wv[u] = __shfl(my_w, sl, kWave);
+      ok[u] = sl < k && row >= 0 && row < T * k;     // rows of d: T * k
+      const float* src = d + (int64_t)(ok[u] ? row : 0) * H + 4 * lane;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        v[u][c] = ok[u] ? *reinterpret_cast<const float4*>(src + 256 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      if (!ok[u]) continue;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        float4 x = v[u][c];
+        if (topk_w) { x.x = wv[u] * x.x; x.y = wv[u] * x.y; x.z = wv[u] * x.z; x.w = wv[u] * x.w; }
+        if (started) {
+          acc[c].x = acc[c].x + x.x; acc[c].y = acc[c].y + x.y; acc[c].z = acc[c].z + x.z; acc[c].w = acc[c].w + x.w;
+        } else {
+          acc[c] = x;
+        }
+      }
+      started = true;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    uint2 o;
+    o.x = f32_to_bf16_rne(acc[c].x) | (f32_to_bf16_rne(acc[c].y) << 16);
+    o.y = f32_to_bf16_rne(acc[c].z) | (f32_to_bf16_rne(acc[c].w) << 16);
+    *reinterpret_cast<uint2*>(y + t * (int64_t)H + 256 * c + 4 * lane) = o;
+  }
+}
+
 // out[r] = x[row_to_tk[r] / k] for every routed row r.
 __global__ __launch_bounds__(256) void permute_gather_kernel(
     const uint16_t* __restrict__ x, int64_t T, int H, int k, const int32_t* __restrict__ offsets, int E,
@@ -169,8 +231,11 @@ NVFP4MOE_API int unpermute_combine(const float* d, int64_t T, int32_t k, int64_t
   if (!d || !tk_to_row || !y) return NVFP4_ERR_NULL;
   if (!aligned16(d) || !aligned16(y)) return NVFP4_ERR_ALIGN;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  unpermute_combine_kernel<<<(unsigned)((T + kRows - 1) / kRows), 256, 0, s>>>(
-      d, T, k, (int)H, tk_to_row, topk_w, y);
+  const unsigned grid = (unsigned)((T + kRows - 1) / kRows);
+  if (H == 1024) unpermute_combine_rows_kernel<4><<<grid, 256, 0, s>>>(d, T, k, tk_to_row, topk_w, y);
+  else if (H == 2048) unpermute_combine_rows_kernel<8><<<grid, 256, 0, s>>>(d, T, k, tk_to_row, topk_w, y);
+  else if (H == 4096) unpermute_combine_rows_kernel<16><<<grid, 256, 0, s>>>(d, T, k, tk_to_row, topk_w, y);
+  else unpermute_combine_kernel<<<grid, 256, 0, s>>>(d, T, k, (int)H, tk_to_row, topk_w, y);
   return launch_status();
 }
 

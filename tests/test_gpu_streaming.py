@@ -79,7 +79,10 @@ def test_swiglu_quantize_skips_rows_past_offsets():
 
 
 @pytest.mark.parametrize("T,E,k,H,weighted,bad", [(4096, 128, 8, 2048, False, False),
-                                                   (37, 16, 4, 264, True, False),
+                                                   (64, 8, 7, 2048, True, True),    # slot pairs, odd k
+                                                   (300, 32, 5, 1024, True, True),  # groups of 4 slots
+                                                   (100, 16, 3, 4096, True, False), # one slot at a time
+                                                   (37, 16, 4, 264, True, False),   # other H: column loop
                                                    (20, 8, 3, 64, True, True)])
 def test_unpermute_combine(T, E, k, H, weighted, bad):
     print(f"[combine] T={T} k={k} H={H} weighted={weighted} invalid={bad}", flush=True)
