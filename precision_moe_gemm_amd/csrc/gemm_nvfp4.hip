@@ -36,8 +36,9 @@
 //   * Decoding is v_cvt_scalef32_pk_f16_fp4 plus one packed FP16 multiply by
 //     the block scale per element pair.
 //   * A tile's epilogue runs after the first barrier of the next tile: its
-//     output stores are then younger than every load that a later K-step
-//     waits for, so no wait has to cover them.
+//     output stores are issued after the loads that this K-step's wait needed,
+//     so the first wait that covers them is the next K-step's, and they have a
+//     whole K-step to drain.
 // Lane half h (lanes 32h..32h+31) of every MFMA takes the elements
 // [32h, 32h+32) of the K-step, i.e. block scales 2h and 2h+1, and feeds 8 of
 // them to each of the 4 MFMA K-slices.  Both operands use the same
