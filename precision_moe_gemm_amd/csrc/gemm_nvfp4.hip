@@ -177,11 +177,16 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// One tile: rows [m0, m0 + rows) of expert e (rows <= BM), columns [n0, n0 + BN).
+// One tile: rows [m0, m0 + rows) of expert e (rows <= BM), columns [n0, n0 + BN),
+// or, for a quarter tile (q = 0..3), columns [n0, n0 + BN / 4) with n0 the
+// whole tile's first column + q BN / 4.
 struct Tile {
   int e, m0, rows, n0;
   int kb0, nk;   // first K-step of the tile's contraction and its K-steps
+  int q;         // -1: a whole tile; 0..3: a column quarter
 };
+constexpr int kQW = BN / 4;              // columns of a quarter tile
+constexpr int kNoTile = 0x7fffffff;      // end of a workgroup's tile sequence
 
 // the expert of m-tile tm: the last e with tile_start[e] <= tm
 __device__ __forceinline__ int expert_of(int tm, const int* tile_start, int E) {
@@ -205,11 +210,20 @@ __device__ __forceinline__ int group_off(const int32_t* __restrict__ offsets, in
   else return min(max(offsets[e], 0), Mg);
 }
 
-template <bool KG>
-__device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_start,
+// Tile L < total is whole tile L; with QT, L >= total is quarter
+// (L - total) % 4 of whole tile (L - total) / 4.
+template <bool KG, bool QT>
+__device__ __forceinline__ Tile tile_at(int L, int total, int n_tiles, const int* tile_start,
                                         const int16_t* mt_expert, int E,
                                         const int32_t* __restrict__ offsets, int Mg,
                                         const int32_t* __restrict__ kofs, int nk) {
+  int q = -1;
+  if constexpr (QT) {
+    if (L >= total) {
+      q = (L - total) & 3;
+      L = (L - total) >> 2;
+    }
+  }
   const int tm = L / n_tiles, tn = L - tm * n_tiles;
   const int lo = mt_expert ? (int)mt_expert[tm] : expert_of(tm, tile_start, E);
   // the values are the same in every lane: keep them in scalar registers
@@ -217,7 +231,8 @@ __device__ __forceinline__ Tile tile_at(int L, int n_tiles, const int* tile_star
   t.e = __builtin_amdgcn_readfirstlane(lo);
   t.m0 = __builtin_amdgcn_readfirstlane(group_off<KG>(offsets, Mg, t.e) + (tm - tile_start[t.e]) * BM);
   t.rows = __builtin_amdgcn_readfirstlane(min(BM, group_off<KG>(offsets, Mg, t.e + 1) - t.m0));
-  t.n0 = tn * BN;
+  t.n0 = tn * BN + (q >= 0 ? q * kQW : 0);
+  t.q = q;
   if constexpr (KG) {
     t.kb0 = __builtin_amdgcn_readfirstlane(min(max(kofs[t.e], 0), nk - 1));
     t.nk = __builtin_amdgcn_readfirstlane(min(max(kofs[t.e + 1] - t.kb0, 1), nk - t.kb0));
@@ -254,7 +269,7 @@ __device__ __forceinline__ float swiglu_f32(float g, float u, float w) {
 // K-tiled weights [K/64][N][32], both over the group's K-steps
 // [kofs[e], kofs[e+1]); its output rows are e Mg .. e Mg + Mg - 1; row scales
 // a_rscales [E][Mg], w_rscales [E][N].
-template <bool KT, bool OB, bool SW, bool KG>
+template <bool KT, bool OB, bool SW, bool KG, bool QT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_bscales,
@@ -265,6 +280,7 @@ void grouped_gemm_kernel(
     const int32_t* __restrict__ kofs, int Mg) {
   static_assert(!SW || (KT && !OB), "the SwiGLU epilogue reads K-tiled weights and writes FP32");
   static_assert(!KG || (KT && !SW), "K-grouped tiles read K-tiled weights");
+  constexpr bool kQuarters = QT && !SW && !OB && !KG;   // quarter tiles (plain FP32 output only)
   __shared__ Smem sm;
   constexpr bool w_tiled = KT;
 
@@ -304,19 +320,47 @@ void grouped_gemm_kernel(
   // XCD-contiguous tile ranges when the grid is a multiple of 8 workgroups
   // (workgroups go to the XCDs round-robin); the range's workgroups take its
   // tiles in turn
-  int begin, end, step;
+  int begin, end, step, r_lo, j;   // j: this workgroup's index in its range [r_lo, end)
   if ((gridDim.x & 7) == 0) {
     const int per = (total + 7) / 8;
     const int xcd = blockIdx.x & 7;
-    begin = xcd * per + (int)(blockIdx.x >> 3);
+    j = (int)(blockIdx.x >> 3);
+    r_lo = xcd * per;
+    begin = r_lo + j;
     end = min(total, (xcd + 1) * per);
     step = gridDim.x >> 3;
   } else {
+    j = blockIdx.x;
+    r_lo = 0;
     begin = blockIdx.x;
     end = total;
     step = gridDim.x;
   }
-  if (begin >= end) return;
+  // With QT (the host's choice for dense, one-group launches), a last round
+  // that would keep at most a quarter of the range's workgroups busy is split
+  // into column quarters, one per workgroup (128 x 128: the
+  // wavefronts' weight decodes and MFMAs shrink with the columns, and every
+  // output element is formed by the same MFMAs in the same order as in a whole
+  // tile).  Quarters have tile indices past the whole tiles.
+  int split = end, quarter = kNoTile;
+  if constexpr (kQuarters) {
+    const int rem = end > r_lo ? (end - r_lo) % step : 0;
+    if (rem > 0 && 4 * rem <= step && total <= (0x7fffffff - 8) / 5) {   // quarter indices stay in int
+      split = end - rem;
+      if ((j >> 2) < rem) quarter = total + 4 * (split + (j >> 2)) + (j & 3);
+    }
+  }
+  // this workgroup's tiles: begin, begin + step, ... below split, then its quarter
+  auto next_tile = [&](int L) __attribute__((always_inline)) -> int {
+    if constexpr (kQuarters) {
+      if (L >= total) return kNoTile;
+      return L + step < split ? L + step : quarter;
+    } else {
+      return L + step < end ? L + step : kNoTile;
+    }
+  };
+  const int first = begin < split ? begin : quarter;
+  if (first == kNoTile) return;
 
   const uint32_t kb = (uint32_t)K / 2, ks = (uint32_t)K / 16;
   const int nk = K / BK;
@@ -331,7 +375,7 @@ void grouped_gemm_kernel(
   // rows or 64 scale dwords.  Activation rows: lane l -> row l/2, 16-byte half
   // l%2 (row-major).  Weight rows: lane l -> row l%32, half l/32, so that a
   // fragment read (16 lanes: 16 rows, one half) covers 256 contiguous bytes.
-  int lL = begin, lk = 0, nkl = nk;   // the loaded tile's K-steps
+  int lL = first, lk = 0, nkl = nk;   // the loaded tile's K-steps
   uint32_t off_c[kCIW], off_s[kSIW];
   // Weight K-step strides: row-major [E][N][K/2] moves 32 code bytes (4 scale
   // bytes) along a row per K-step; the K-tiled layout [E][K/64][N][32] moves
@@ -357,15 +401,19 @@ void grouped_gemm_kernel(
                         : wave < 6 ? (uint32_t)offsetof(Stage, ws) + (uint32_t)(wave - 4) * 1024u
                                    : (uint32_t)offsetof(Stage, as) + (uint32_t)(wave - 6) * 256u;
   uint32_t vo0 = 0, vo1 = 0, vo2 = 0;
-  // weight row of tile column c (callers pass c with c % 4 == 0 or a whole
+  // weight row of stage column c (callers pass c with c % 4 == 0 or a whole
   // 32-column group, so 4 consecutive columns map to 4 consecutive rows);
-  // plain tiles: row n0 + c, kept inside the weight matrix by `cap`
+  // plain tiles: row n0 + c, kept inside the weight matrix by `cap`.  A
+  // quarter tile puts its column group g at the stage's 32-column groups 2g
+  // and 2g + 8, where wavefronts g and g + 4 find it as their fragment 0 (the
+  // odd groups repeat it and are not used).
   auto wcol = [&](const Tile& t, int c, int cap) __attribute__((always_inline)) -> int {
     if constexpr (SW) return ((c >> 5) & 1) * I + (t.n0 >> 1) + ((c >> 6) << 5) + (c & 31);
+    else if constexpr (kQuarters) return min(t.n0 + (t.q >= 0 ? ((c >> 1) & 96) + (c & 31) : c), cap);
     else return min(t.n0 + c, cap);
   };
   auto set_load_tile = [&](int L) __attribute__((always_inline)) {
-    const Tile t = tile_at<KG>(L, n_tiles, sm.tile_start, mt_tab, E, offsets, Mg, kofs, nk);
+    const Tile t = tile_at<KG, kQuarters>(L, total, n_tiles, sm.tile_start, mt_tab, E, offsets, Mg, kofs, nk);
     nkl = t.nk;
     if constexpr (KT) {
       const int m_last = t.m0 + t.rows - 1;
@@ -395,7 +443,7 @@ void grouped_gemm_kernel(
       if (q < BM / 32) {
         off_c[u] = (uint32_t)min(t.m0 + 32 * q + (lane >> 1), m_last) * kb + half * 16;
       } else {
-        const uint32_t n = (uint32_t)min(t.n0 + 32 * (q - BM / 32) + (lane & 31), N - 1);
+        const uint32_t n = (uint32_t)wcol(t, 32 * (q - BM / 32) + (lane & 31), N - 1);
         const uint32_t wh = (lane >> 5) * 16;
         off_c[u] = w_tiled ? ((uint32_t)t.e * nk * N + n) * kRowB + wh
                            : ((uint32_t)t.e * N + n) * kb + wh;
@@ -407,7 +455,7 @@ void grouped_gemm_kernel(
       if (q < 2) {
         off_s[u] = (uint32_t)min(t.m0 + 64 * q + lane, m_last) * ks;
       } else {
-        const uint32_t n = (uint32_t)min(t.n0 + 64 * (q - 2) + lane, N - 1);
+        const uint32_t n = (uint32_t)wcol(t, 64 * (q - 2) + lane, N - 1);
         off_s[u] = w_tiled ? ((uint32_t)t.e * nk * N + n) * kScB : ((uint32_t)t.e * N + n) * ks;
       }
     }
@@ -415,7 +463,7 @@ void grouped_gemm_kernel(
   // issues the loads of the cursor's K-step into stage S and advances the
   // cursor; returns the number of load instructions this wavefront issued
   auto issue_loads = [&](Stage& S) __attribute__((always_inline)) -> int {
-    if (lL >= end) return 0;
+    if (lL == kNoTile) return 0;
     if constexpr (KT) {
       const uint32_t ls = lds_st + (uint32_t)((uintptr_t)(lds_void*)&S - (uintptr_t)(lds_void*)&sm.st[0]);
       lds_dma16_at(src0, (uint32_t)lk * step0 + vo0, ls + ldo0);
@@ -424,8 +472,8 @@ void grouped_gemm_kernel(
       else lds_dma4_at(src2, (uint32_t)lk * step2 + vo2, ls + ldo2);
       if (++lk == nkl) {
         lk = 0;
-        lL += step;
-        if (lL < end) set_load_tile(lL);
+        lL = next_tile(lL);
+        if (lL != kNoTile) set_load_tile(lL);
       }
       return 3;
     }
@@ -445,8 +493,8 @@ void grouped_gemm_kernel(
     }
     if (++lk == nkl) {
       lk = 0;
-      lL += step;
-      if (lL < end) set_load_tile(lL);
+      lL = next_tile(lL);
+      if (lL != kNoTile) set_load_tile(lL);
     }
     return n_loads;
   };
@@ -466,10 +514,11 @@ void grouped_gemm_kernel(
     *reinterpret_cast<half8*>(A16 + a16_off(drow, 2 * dq + 0)) = decode8(da.x, s0);
     *reinterpret_cast<half8*>(A16 + a16_off(drow, 2 * dq + 1)) = decode8(da.y, s0);
   };
-  // weight fragments: fragment f of this wavefront = W rows 64 wave + 32 f +
-  // (lane % 32); the lane's 32 elements [32h, 32h+32) of the K-step are 16
-  // code bytes (word s = the 8 elements of MFMA slice s) and block scales 2h,
-  // 2h+1 (slices 0-1 and 2-3)
+  // weight fragments: fragment f of this wavefront = the stage's W rows
+  // 64 wave + 32 f + (lane % 32) (for a quarter tile, fragment 0 holds the
+  // wavefront's column group and fragment 1 is not used); the lane's 32
+  // elements [32h, 32h+32) of the K-step are 16 code bytes (word s = the 8
+  // elements of MFMA slice s) and block scales 2h, 2h+1 (slices 0-1 and 2-3)
   uint4 rb[FB];
   uint32_t xb[FB];
   auto read_b = [&](const Stage& S) __attribute__((always_inline)) {
@@ -485,7 +534,7 @@ void grouped_gemm_kernel(
   };
 
   // ---------------------------------------------------------------- prologue
-  set_load_tile(begin);
+  set_load_tile(first);
   issue_loads(sm.st[0]);
   issue_loads(sm.st[1]);
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
@@ -512,16 +561,22 @@ void grouped_gemm_kernel(
   // interleaved.  A fragments are read one slice ahead.  The next K-step's
   // stage is read and decoded even when there is none: the reads stay inside
   // LDS and what they produce is never used.  FULL: all row fragments hold
-  // rows; otherwise fragments at or past fa_eff are skipped.
-  auto mma_step = [&](auto full_tag, int fa_eff) __attribute__((always_inline)) {
+  // rows; otherwise fragments at or past fa_eff are skipped.  Q: a quarter
+  // tile (the wavefront's rows 64 (wave / 4) .. + 63, weight fragment 0).
+  // The next K-step's weight fragments are read and their first slice decoded
+  // in full: the layout is the same for both kinds of tile.
+  auto mma_step = [&](auto full_tag, int fa_eff, auto q_tag) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full_tag)::value;
+    constexpr bool Q = decltype(q_tag)::value;
+    constexpr int fa = Q ? 2 : FA, fb = Q ? 1 : FB;
+    const int r0 = Q ? 64 * (wave >> 2) : 0;
     const uint8_t* A16 = sm.a16[ab];
     uint8_t* A16n = sm.a16[ab ^ 1];
     const Stage& Sn = sm.st[sc == kStages - 1 ? 0 : sc + 1];
     half8 av[FA], bn[FB];
 #pragma unroll
-    for (int i = 0; i < FA; ++i)
-      av[i] = *reinterpret_cast<const half8*>(A16 + a16_off(32 * i + l32, 4 * h));
+    for (int i = 0; i < fa; ++i)
+      av[i] = *reinterpret_cast<const half8*>(A16 + a16_off(r0 + 32 * i + l32, 4 * h));
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s == 0) read_a(Sn);
@@ -529,7 +584,7 @@ void grouped_gemm_kernel(
       // B values of the next slice (of the next K-step after slice 3)
       if (s < 3) {
 #pragma unroll
-        for (int j = 0; j < FB; ++j)
+        for (int j = 0; j < fb; ++j)
           bn[j] = decode8(word(rb[j], s + 1), scale_pair(s + 1 < 2 ? (xb[j] & 0xFF) : (xb[j] >> 8)));
       }
       if (s == 2) read_b(Sn);
@@ -538,17 +593,17 @@ void grouped_gemm_kernel(
         for (int j = 0; j < FB; ++j) bn[j] = decode8(rb[j].x, scale_pair(xb[j] & 0xFF));
       }
 #pragma unroll
-      for (int i = 0; i < FA; ++i) {
+      for (int i = 0; i < fa; ++i) {
         const half8 a = av[i];
-        if (s < 3) av[i] = *reinterpret_cast<const half8*>(A16 + a16_off(32 * i + l32, 4 * h + s + 1));
+        if (s < 3) av[i] = *reinterpret_cast<const half8*>(A16 + a16_off(r0 + 32 * i + l32, 4 * h + s + 1));
         if (FULL || i < fa_eff) {
 #pragma unroll
-          for (int j = 0; j < FB; ++j)
+          for (int j = 0; j < fb; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], a, acc[i][j], 0, 0, 0);
         }
       }
 #pragma unroll
-      for (int j = 0; j < FB; ++j) bv[j] = bn[j];
+      for (int j = 0; j < (s < 3 ? fb : FB); ++j) bv[j] = bn[j];
     }
   };
 
@@ -585,6 +640,48 @@ void grouped_gemm_kernel(
   auto epilogue = [&](const Tile& t, int rb) __attribute__((always_inline)) {
     const float* rs_a = sm.rs[rb];
     const float* rs_w = sm.rs[rb] + BM;
+    if constexpr (kQuarters) {
+      if (t.q >= 0) {
+        // a quarter tile: the wavefront's fragments are rows r0 + 32 i (i < 2)
+        // and columns c0 .. c0 + 31 of the quarter (the stage's columns
+        // 64 wave .., whose row scales sit there too), staged and stored as below
+        const int r0 = 64 * (wave >> 2), c0 = 32 * (wave & 3);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<float*>(c) + (int64_t)t.m0 * N, (short)0, t.rows * N * 4, 0x00020000);
+        uint8_t* stq = sm.stg[wave];
+        const int srow = lane >> 3, sch = lane & 7;
+        uint32_t srowN = (uint32_t)(srow * N);
+        asm volatile("" : "+v"(srowN));
+        float4 swv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          swv[q] = *reinterpret_cast<const float4*>(&rs_w[WN * wave + 8 * q + 4 * h]);
+        const int n = t.n0 + c0 + 4 * sch;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const float sq = rs_a[r0 + 32 * i + l32];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float4 o;
+            o.x = (acc[i][0][4 * q + 0] * sq) * swv[q].x;
+            o.y = (acc[i][0][4 * q + 1] * sq) * swv[q].y;
+            o.z = (acc[i][0][4 * q + 2] * sq) * swv[q].z;
+            o.w = (acc[i][0][4 * q + 3] * sq) * swv[q].w;
+            *reinterpret_cast<float4*>(stq + l32 * 128 + (((2 * q + h) ^ (l32 & 7)) << 4)) = o;
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 8 * r + srow;
+            const float4 v = *reinterpret_cast<const float4*>(stq + row * 128 + ((sch ^ (row & 7)) << 4));
+            const uint32_t off =
+                n < N ? ((uint32_t)((r0 + 32 * i + 8 * r) * N) + srowN + (uint32_t)n) * 4u : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rq, off, 0, kNonTemporal);
+          }
+          acc[i][0] = floatx16{};
+        }
+        return;
+      }
+    }
     float sa[FA];
 #pragma unroll
     for (int i = 0; i < FA; ++i) sa[i] = rs_a[32 * i + l32];
@@ -747,8 +844,8 @@ void grouped_gemm_kernel(
   // scales landed with the loads it waited for, and the tile's own row scales
   // go to the other buffer.
   int rbuf = 0;
-  auto run_tile = [&](auto full_tag, int fa_eff, const Tile& t) __attribute__((always_inline)) {
-    mma_step(full_tag, fa_eff);   // K-step 0: its wait, barrier and loads are done by the caller
+  auto run_tile = [&](auto full_tag, int fa_eff, const Tile& t, auto q_tag) __attribute__((always_inline)) {
+    mma_step(full_tag, fa_eff, q_tag);   // K-step 0: its wait, barrier and loads are done by the caller
     sc = sc == kStages - 1 ? 0 : sc + 1;
     ab ^= 1;
     for (int kt = 1; kt < t.nk; ++kt) {
@@ -756,23 +853,34 @@ void grouped_gemm_kernel(
       lds_barrier();
       if (kt == t.nk - 1) issue_rscales(t, rbuf);
       n_last = issue_loads(sm.st[sc]);
-      mma_step(full_tag, fa_eff);
+      mma_step(full_tag, fa_eff, q_tag);
       sc = sc == kStages - 1 ? 0 : sc + 1;
       ab ^= 1;
     }
   };
 
-  Tile prev{0, 0, 0, 0};
-  for (int L = begin; L < end; L += step) {
-    const Tile t = tile_at<KG>(L, n_tiles, sm.tile_start, mt_tab, E, offsets, Mg, kofs, nk);
-    const int fa_eff = (t.rows + 31) >> 5;
+  Tile prev{0, 0, 0, 0, 0, 0, -1};
+  for (int L = first; L != kNoTile; L = next_tile(L)) {
+    const Tile t = tile_at<KG, kQuarters>(L, total, n_tiles, sm.tile_start, mt_tab, E, offsets, Mg, kofs, nk);
     wait_vmcnt(n_last);
     lds_barrier();
     epilogue(prev, rbuf ^ 1);   // before the first tile: no rows, every store is dropped
     if (t.nk == 1) issue_rscales(t, rbuf);
     n_last = issue_loads(sm.st[sc]);
-    if (fa_eff == FA) run_tile(std::true_type{}, FA, t);
-    else run_tile(std::false_type{}, fa_eff, t);
+    bool done = false;
+    if constexpr (kQuarters) {
+      if (t.q >= 0) {   // the wavefront's rows of a quarter: 64 (wave / 4) .. + 63
+        const int fq = min(2, max(0, (t.rows - 64 * (wave >> 2) + 31) >> 5));
+        if (fq == 2) run_tile(std::true_type{}, 2, t, std::true_type{});
+        else run_tile(std::false_type{}, fq, t, std::true_type{});
+        done = true;
+      }
+    }
+    if (!done) {
+      const int fa_eff = (t.rows + 31) >> 5;
+      if (fa_eff == FA) run_tile(std::true_type{}, FA, t, std::false_type{});
+      else run_tile(std::false_type{}, fa_eff, t, std::false_type{});
+    }
     prev = t;
     rbuf ^= 1;
   }
@@ -816,15 +924,18 @@ extern "C" NVFP4MOE_API int nvfp4_grouped_gemm(const uint8_t* a_codes, const uin
   int64_t grid = max_tiles < 256 ? max_tiles : 256;
   if (grid >= 8) grid &= ~7ll;
   hipStream_t s = static_cast<hipStream_t>(stream);
-#define GG_LAUNCH(KT, OB)                                                                    \
-  g5::grouped_gemm_kernel<KT, OB, false, false><<<(unsigned)grid, g5::kThreads, 0, s>>>(      \
+#define GG_LAUNCH(KT, OB, QT)                                                                    \
+  g5::grouped_gemm_kernel<KT, OB, false, false, QT><<<(unsigned)grid, g5::kThreads, 0, s>>>(  \
       a_codes, a_bscales, a_rscales, expert_offsets, E, w_codes, w_bscales, w_rscales, (int)N, \
       (int)K, c, nullptr, nullptr, 0, nullptr, (int)R_cap)
-  const bool kt = w_layout == NVFP4_W_KTILED, ob = c_dtype == NVFP4_OUT_BF16;
-  if (kt && !ob) GG_LAUNCH(true, false);
-  else if (kt) GG_LAUNCH(true, true);
-  else if (!ob) GG_LAUNCH(false, false);
-  else GG_LAUNCH(false, true);
+  // quarter tiles for a sparse last round: dense (one-group) FP32 launches
+  const bool kt = w_layout == NVFP4_W_KTILED, ob = c_dtype == NVFP4_OUT_BF16, qt = E == 1;
+  if (kt && !ob && qt) GG_LAUNCH(true, false, true);
+  else if (kt && !ob) GG_LAUNCH(true, false, false);
+  else if (kt) GG_LAUNCH(true, true, false);
+  else if (!ob && qt) GG_LAUNCH(false, false, true);
+  else if (!ob) GG_LAUNCH(false, false, false);
+  else GG_LAUNCH(false, true, false);
 #undef GG_LAUNCH
   return launch_status();
 }

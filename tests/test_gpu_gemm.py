@@ -133,6 +133,57 @@ def test_rows_are_batch_invariant():
         assert np.array_equal(part, full[t0:t1])
 
 
+def _oracle_rows(a_bits, off, w_bits, rows):
+    """oracle C rows (with their bounds) of row-quantised activations a_bits"""
+    a_ref = oq.quantize_rows_bf16(a_bits)
+    return og.grouped_gemm_ref(*a_ref, off, *quantize_weights_oracle(w_bits), rows=rows)
+
+
+def test_quarter_tiles_dense():
+    """A last round that would keep at most a quarter of a range's workgroups
+    busy is split into 128-column quarter tiles.  Dense 4096 x 5120 (320 tiles
+    on 256 workgroups: the last 8 of every 40-tile range become 32 quarters).
+    The quarters must give the bits of whole tiles (two half-height launches,
+    whose single round has no quarters) and the oracle's values on rows of
+    quartered and whole m-tiles."""
+    print("[gemm] quarter tiles: dense 4096x5120, K 256", flush=True)
+    M, K, N = 4096, 256, 5120
+    x = W.activations(M, K, config=44)
+    w_bits = W.gaussian_bf16((1, N, K), 0.02, 44, 1)
+    a = pmg.nvfp4_quantize_rows(bf16_dev(x))
+    w = quantize_weights_gpu(w_bits)
+    full = host(pmg.nvfp4_grouped_gemm(*a, dev(np.array([0, M], np.int32)), *w))
+    for lo, hi in [(0, 2048), (2048, 4096)]:
+        sub = tuple(v[lo:hi].clone() for v in a)
+        part = host(pmg.nvfp4_grouped_gemm(*sub, dev(np.array([0, hi - lo], np.int32)), *w))
+        assert np.array_equal(part.view(np.int32), full[lo:hi].view(np.int32)), f"rows {lo}..{hi}"
+    # m-tile 3 (rows 384..511) has quartered columns 1024.., m-tile 0 none
+    rows = np.unique(np.concatenate([np.arange(0, 40), np.arange(384, 512), np.arange(4060, 4096)]))
+    ref, bound = _oracle_rows(x, np.array([0, M], np.int64), w_bits, rows)
+    print("  err/bound", assert_within(full[rows], ref, bound, "quarters dense"))
+
+
+def test_quarter_tiles_dense_ragged():
+    """Quarter tiles with rows missing: dense 4000 x 5120, K 128, K-tiled weights
+    (m-tile 31 holds 32 rows, so in its quarters one wavefront row half has a
+    single 32-row fragment and the other none).  Bit-identical to two half-height
+    launches without quarters; every row of m-tiles 3 and 31 against the oracle."""
+    print("[gemm] quarter tiles: dense 4000x5120, K 128, K-tiled", flush=True)
+    M, K, N = 4000, 128, 5120
+    x = W.activations(M, K, config=45)
+    w_bits = W.gaussian_bf16((1, N, K), 0.02, 45, 1)
+    a = pmg.nvfp4_quantize_rows(bf16_dev(x))
+    w = quantize_weights_gpu_tiled(w_bits)
+    full = host(pmg.nvfp4_grouped_gemm(*a, dev(np.array([0, M], np.int32)), *w))
+    for lo, hi in [(0, 2000), (2000, 4000)]:
+        sub = tuple(v[lo:hi].clone() for v in a)
+        part = host(pmg.nvfp4_grouped_gemm(*sub, dev(np.array([0, hi - lo], np.int32)), *w))
+        assert np.array_equal(part.view(np.int32), full[lo:hi].view(np.int32)), f"rows {lo}..{hi}"
+    rows = np.concatenate([np.arange(384, 512), np.arange(3968, 4000)])
+    ref, bound = _oracle_rows(x, np.array([0, M], np.int64), w_bits, rows)
+    print("  err/bound", assert_within(full[rows], ref, bound, "quarters ragged"))
+
+
 def test_repeated_calls_are_identical():
     """Back-to-back calls (ragged experts, more tiles than workgroups) give
     bit-identical results."""
