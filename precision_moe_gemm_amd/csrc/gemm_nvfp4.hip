@@ -50,6 +50,12 @@
 // The grid is persistent: each workgroup walks tiles of a contiguous range
 // owned by its XCD (workgroups go to the 8 XCDs round-robin), m-tile major,
 // so the A rows and an expert's weights are reused from that XCD's L2.
+// Dense (one-group) launches split a last round that would keep at most a
+// quarter of a range's workgroups busy into 128 x 128 quarter tiles, one per
+// workgroup: wavefront w takes rows 64 (w / 4) .. + 63 and column group w % 4
+// with the same MFMAs (so the same bits) as in a whole tile, and a quarter
+// costs about three quarters of a whole tile (its loads, barriers and
+// activation decode do not shrink).
 #include "common.h"
 
 #include <type_traits>
