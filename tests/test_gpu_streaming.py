@@ -37,7 +37,12 @@ def _gu(R, I, seed, scale=2.0):
 
 
 @pytest.mark.parametrize("T,E,k,I,weighted", [(4096, 128, 8, 768, True), (100, 8, 2, 768, False),
-                                               (50, 4, 2, 48, True), (64, 2, 1, 4096, True)])
+                                               (50, 4, 2, 48, True), (64, 2, 1, 4096, True),
+                                               # rows of one chunk without the split tail (several
+                                               # rows per wavefront), of two chunks without it
+                                               # (lanes past the row end; a whole last chunk)
+                                               (2048, 16, 4, 384, True), (300, 8, 4, 1008, False),
+                                               (512, 8, 2, 1024, True)])
 def test_swiglu_quantize(T, E, k, I, weighted):
     print(f"[swiglu_quantize] T={T} E={E} k={k} I={I} weighted={weighted}", flush=True)
     ids, tw, off, r2t, t2r = _routing(T, E, k, "uniform", 50)
