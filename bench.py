@@ -442,7 +442,12 @@ def comparisons(t, gemm_flops):
         against the step's BF16 ones;
       fused_swiglu_gate_up: the step's gate_up with the FP32 SwiGLU in its
         epilogue + the FP32-row quantiser, against the plain gate_up GEMM + the
-        float64 SwiGLU-quantise pass."""
+        float64 SwiGLU-quantise pass;
+      ep8_shard: one GPU's share of 8-way expert parallelism (16 local experts
+        whose rows come from every GPU's tokens, about 2048 each): the step's
+        32768 routed rows and the first 16 experts' weights, the 128 experts' row
+        counts summed in groups of 8 as the local experts' counts, against the
+        step's own expert GEMMs."""
     import torch
     import precision_moe_gemm_amd as pmg
     x, dy, ids, E, k, I, H = t["x"], t["dy"], t["ids"], t["E"], t["k"], t["I"], t["H"]
@@ -471,6 +476,22 @@ def comparisons(t, gemm_flops):
         "nvfp4_down_gemm": {"us": round(us_nv_dn, 2), "TFLOPs": tf("down_gemm", us_nv_dn)},
         "nvfp4_gemms_speedup": round((us_gu + us_dn) / (us_nv_gu + us_nv_dn), 3)}
     del gu_bf, dn_bf, h16
+    # the per-GPU share of 8-way expert parallelism
+    counts = (off[1:] - off[:-1]).view(E // 8, 8).sum(dim=1)
+    off_s = torch.zeros(E // 8 + 1, dtype=torch.int32, device=dev)
+    off_s[1:] = torch.cumsum(counts, 0).to(torch.int32)
+    q_gu16 = tuple(v[: E // 8].contiguous() for v in t["q_gu"])
+    q_d16 = tuple(v[: E // 8].contiguous() for v in t["q_d"])
+    us_s_gu = _time_op(lambda: pmg.nvfp4_grouped_gemm(*a[:3], off_s, *q_gu16, c=t["gu"]))
+    us_s_dn = _time_op(lambda: pmg.nvfp4_grouped_gemm(a2["codes"], a2["bscales"], a2["rscales"], off_s, *q_d16,
+                                                      c=t["dn"]))
+    cnt_h = counts.cpu().numpy()
+    out["ep8_shard"] = {
+        "gate_up_gemm": {"us": round(us_s_gu, 2), "TFLOPs": tf("gate_up_gemm", us_s_gu)},
+        "down_gemm": {"us": round(us_s_dn, 2), "TFLOPs": tf("down_gemm", us_s_dn)},
+        "layer_gate_up_gemm_us": round(us_nv_gu, 2), "layer_down_gemm_us": round(us_nv_dn, 2),
+        "local_experts": E // 8, "rows_per_local_expert": [int(cnt_h.min()), int(cnt_h.max())]}
+    del q_gu16, q_d16
     # NVFP4 input gradient against the step's BF16 dgrad GEMMs
     us_bf_dd = _time_op(lambda: pmg.bf16_grouped_gemm_gather(dy, r2t, k, off, t["wd"], pmg.W_KN, c=t["dh"]))
     us_bf_dg = _time_op(lambda: pmg.bf16_grouped_gemm(t["dgu"], off, t["wgu"], pmg.W_KN, c=t["dx_perm"]))
