@@ -351,7 +351,10 @@ NVFP4MOE_API int nvfp4_grouped_gemm_wgrad(const uint8_t* a_codes, const uint8_t*
  *   topk_w    float [T*k] router weight of (t, slot) (NULL: weight 1)
  *   row_to_tk int32 [R_cap] from nvfp4_quantize_permute (needed if topk_w; an entry
  *             outside [0, R_cap) gives that row the router weight 0)
- *   h = float32( ((g / (1 + exp(-g))) * u) * w ), evaluated in FP64
+ *   h = float32( ((g / (1 + exp(-g))) * u) * w ), evaluated in FP64 (g times the
+ *             sigmoid from the library's own exp and a Newton-refined reciprocal: within
+ *             2^-50 relative of the exact value, so h can differ from the correctly
+ *             rounded float32 only where that value lies next to a rounding midpoint)
  *   codes [R_cap][I/2], bscales [R_cap][I/16], rscales [R_cap]: NVFP4 of h
  *   h_out     float [R_cap][I] (NULL: not written)
  * Requires I % 16 == 0, 16 <= I <= NVFP4MOE_MAX_K.
@@ -424,9 +427,9 @@ NVFP4MOE_API int bf16_grouped_gemm_gather(const uint16_t* a, int64_t T, const in
 /*
  * swiglu_backward - gradient of h = w * silu(g) * u with respect to g and u:
  *   t = dh * w;  du = t * silu(g);  dg = (t * u) * (sig * (1 + g * (1 - sig)))
- * with sig = 1 / (1 + exp(-g)), silu(g) = g / (1 + exp(-g)), in FP64 (sig from a
- * Newton-refined reciprocal, silu = g * sig: within a few FP64 ulps of the
- * quotients); each result rounded once to bf16 (nearest even).
+ * with sig = 1 / (1 + exp(-g)), silu(g) = g / (1 + exp(-g)), in FP64 (sig as in
+ * swiglu_quantize, silu = g * sig: within 2^-50 relative of the quotients); each
+ * result rounded once to bf16 (nearest even).
  *   gu float [R_cap][2I] (forward gate_up output); dh float [R_cap][I]
  *   topk_w / row_to_tk as in swiglu_quantize (NULL topk_w: w = 1)
  *   dgu bf16 bits [R_cap][2I]: [0, I) = dg, [I, 2I) = du

@@ -135,12 +135,14 @@ __global__ __launch_bounds__(256) void permute_gather_kernel(
     *reinterpret_cast<uint4*>(dst + base) = *reinterpret_cast<const uint4*>(src + base);
 }
 
-// Gradient of h = w * silu(g) * u in float64 (sigmoid from a refined
-// reciprocal, silu = g * sigmoid), each output rounded once to bf16.
+// Gradient of h = w * silu(g) * u in float64 (sigmoid_f64, within 2^-50 of the
+// sigmoid; silu = g * sigmoid), each output rounded once to bf16.
 __global__ __launch_bounds__(256) void swiglu_backward_kernel(
     const float* __restrict__ gu, const float* __restrict__ dh, int64_t R_cap, int I,
     const int32_t* __restrict__ offsets, int E, const float* __restrict__ topk_w,
     const int32_t* __restrict__ row_to_tk, uint16_t* __restrict__ dgu) {
+  __shared__ double exp2_tab[64];
+  stage_exp2_table(exp2_tab);
   const int64_t r = (int64_t)blockIdx.x * kRows + (threadIdx.x >> 6);
   if (r >= offsets[E] || r >= R_cap) return;
   float w = 1.0f;
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(
         const double g = gs[j + q], u = us[j + q];
         double t = ds[j + q];
         if (topk_w) t = t * (double)w;
-        const double sig = recip_f64(1.0 + exp(-g));
+        const double sig = sigmoid_f64(gs[j + q], exp2_tab);
         const double silu = g * sig;
         const double du = t * silu;
         const double dg = (t * u) * (sig * (1.0 + g * (1.0 - sig)));

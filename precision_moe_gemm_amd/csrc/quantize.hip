@@ -683,6 +683,8 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
     const float* __restrict__ topk_w, const int32_t* __restrict__ row_to_tk,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ bscales, float* __restrict__ rscales,
     float* __restrict__ h_out) {
+  __shared__ double exp2_tab[64];
+  stage_exp2_table(exp2_tab);
   const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (r >= offsets[E] || r >= R_cap) return;
   const int lane = lane_id();
@@ -692,11 +694,10 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(
     const int32_t i = row_to_tk[r];
     w = (i >= 0 && i < R_cap) ? topk_w[i] : 0.0f;
   }
-  // SwiGLU of one element: float64, in the order of the definition, rounded once
+  // SwiGLU of one element: float64 (silu(g) as g times the sigmoid), then
+  // times u and the router weight, rounded once to float
   auto swiglu = [&](float gf, float uf) __attribute__((always_inline)) -> float {
-    const double g = gf;
-    const double e = exp(-g);
-    double hv = (g / (1.0 + e)) * (double)uf;
+    double hv = ((double)gf * sigmoid_f64(gf, exp2_tab)) * (double)uf;
     if (topk_w) hv = hv * (double)w;
     return (float)hv;
   };

@@ -102,7 +102,8 @@ def sample_rows(offsets: np.ndarray, experts, extra: int, seed: int):
 
 
 def bf16_midpoint_adjacent(x64, rel=2.0 ** -40):
-    """True where x lies within rel*|x| of a bf16 rounding midpoint (neighbours from the bit pattern)."""
+    """True where x lies within rel*|x| of a bf16 rounding midpoint (neighbours from the bit pattern);
+    exact zeros are compared as they are, sign included."""
     b = of.round_to_bf16(x64).astype(np.int32)
     mag = b & 0x7FFF
     sign = b & 0x8000
@@ -110,7 +111,8 @@ def bf16_midpoint_adjacent(x64, rel=2.0 ** -40):
     up = of.bf16_to_f32((sign | np.minimum(mag + 1, 0x7F7F)).astype(np.uint16)).astype(np.float64)
     dn = of.bf16_to_f32((sign | np.maximum(mag - 1, 0)).astype(np.uint16)).astype(np.float64)
     dist = np.minimum(np.abs(x64 - (q + up) / 2), np.abs(x64 - (q + dn) / 2))
-    return dist <= rel * np.maximum(np.abs(x64), 1e-300)
+    # an exact zero is never near a midpoint (below, dn clamps to zero itself)
+    return (dist <= rel * np.maximum(np.abs(x64), 1e-300)) & (x64 != 0)
 
 
 class BF16Experts:

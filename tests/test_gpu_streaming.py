@@ -1,9 +1,9 @@
 """GPU parity: weighted SwiGLU + quantise, combine, gather, SwiGLU backward, BF16 grouped GEMM.
 
-SwiGLU forward/backward: the GPU evaluates in float64 like the oracle; its
-exp() may differ from numpy's in the last float64 bit, and the backward takes
-the sigmoid from a refined reciprocal and multiplies where the oracle divides,
-so its float64 values may differ from the oracle's by a few ulps.  That can
+SwiGLU forward/backward: the GPU evaluates in float64 like the oracle, with
+its own exp (table and polynomial) and a refined reciprocal, multiplying where
+the oracle divides, so its float64 values may differ from the oracle's by a
+few ulps.  That can
 change a float32 (bf16) rounding only when the oracle's float64 value lies
 within a few float64 ulps of a rounding midpoint.  Those elements (found by
 the oracle alone) are listed; every other element must match bit for bit.
@@ -129,6 +129,77 @@ def test_swiglu_backward(T, E, k, I, weighted):
     got = bf16_host(dgu)
     amb = _bf16_midpoint_adjacent(d64)
     diff = got != ref_bits
+    assert not np.any(diff & ~amb), f"{int((diff & ~amb).sum())} bf16 values differ"
+
+
+# g values at the edges of the float64 exp: zeros, tiny values, both sides of
+# exp(-g) overflowing (g near -709.78) and of it underflowing to 0 (g near
+# 745.13), far beyond both, and the float32 extremes
+_G_SPECIAL = np.array([0.0, -0.0, 1e-30, -1e-30, 0.5, -0.5, 20.0, -20.0, 40.0, -40.0, 87.5, -87.5,
+                       88.75, -88.75, 103.9, -103.9, 500.0, -500.0, 709.75, -709.75, 709.7826, -709.7826,
+                       709.7828, -709.7828, 710.0, -710.0, 745.0, -745.0, 745.2, -745.2, 746.0, -746.0,
+                       800.0, -800.0, 1e10, -1e10, 3e38, -3e38], np.float32)
+
+
+def _gu_special(R, I, seed):
+    """Rows whose first gate values are _G_SPECIAL (rotated per row), the rest
+    Gaussian; up values of several magnitudes, capped so |g u| stays finite."""
+    gu = _gu(R, I, seed)
+    n = len(_G_SPECIAL)
+    for r in range(R):
+        gu[r, :n] = np.roll(_G_SPECIAL, r)
+    u_mag = np.array([1.0, -1.0, 1e-20, 1e-39, 0.0, -0.0, 1e20, 3.0], np.float32)
+    gu[:, I:I + n] = u_mag[np.arange(R) % len(u_mag)][:, None]
+    big = np.abs(gu[:, :I].astype(np.float64) * gu[:, I:].astype(np.float64)) > 1e37
+    gu[:, I:][big] = np.float32(0.25)
+    return gu
+
+
+def test_swiglu_quantize_special_values():
+    """h at the edges of exp's range (see _G_SPECIAL), bit for bit off float32 midpoints."""
+    R, I = 16, 512
+    gu = _gu_special(R, I, 64)
+    off = np.array([0, 7, R], np.int32)
+    w_rows = np.linspace(0.05, 1.0, R).astype(np.float32)
+    r2t = np.arange(R, dtype=np.int32)
+    codes, bsc, rsc, h = pmg.swiglu_quantize(dev(gu), dev(off), dev(w_rows), dev(r2t), h_out=True)
+    torch.cuda.synchronize()
+    rc, rb, rs, rh, amb = osw.swiglu_quantize_ref(gu, w_rows)
+    gh = host(h)
+    assert np.all(np.isfinite(rh))
+    same = gh.view(np.uint32) == rh.view(np.uint32)
+    assert np.all(same | amb), f"h differs at {np.argwhere(~(same | amb))[:5].tolist()}"
+    oc_, ob_, os_ = oq.quantize_rows_f32(gh)
+    assert np.array_equal(host(codes), oc_) and np.array_equal(host(bsc), ob_)
+    assert np.array_equal(host(rsc).view(np.uint32), os_.view(np.uint32))
+
+
+def test_swiglu_backward_special_values():
+    """dG and dU at the edges of exp's range, and output gradients whose results
+    round into bf16 subnormals or past the bf16 range, bit for bit off bf16
+    midpoints (NaN where the oracle has NaN, from g = +-inf)."""
+    R, I = 16, 512
+    gu = _gu_special(R, I, 65)
+    gu[0, 100], gu[1, 101] = np.inf, -np.inf
+    dh = (W.rng(65, 33).standard_normal((R, I)) * 0.1).astype(np.float32)
+    dh[:, 40:48] = np.array([1e-40, -1e-40, 3e-39, 1e-38, 1e38, -1e38, 3e38, 1e-45], np.float32)
+    off = np.array([0, 5, R], np.int32)
+    w_rows = np.linspace(0.05, 1.0, R).astype(np.float32)
+    r2t = np.arange(R, dtype=np.int32)
+    dgu = pmg.swiglu_backward(dev(gu), dev(dh), dev(off), dev(w_rows), dev(r2t))
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref_bits, d64 = osw.swiglu_backward_ref(gu, dh, w_rows)
+        amb = _bf16_midpoint_adjacent(d64)
+    got = bf16_host(dgu)
+    nan_ref = np.isnan(d64)
+    assert nan_ref.any()
+    nan_got = (got & 0x7F80) == 0x7F80
+    nan_got &= (got & 0x7F) != 0
+    assert np.array_equal(nan_got, nan_ref)
+    sub = (np.abs(d64) < 2.0 ** -126) & (d64 != 0)
+    assert sub.any() and (np.abs(d64[~nan_ref]) >= 2.0 ** 128).any()
+    diff = (got != ref_bits) & ~nan_ref
     assert not np.any(diff & ~amb), f"{int((diff & ~amb).sum())} bf16 values differ"
 
 
