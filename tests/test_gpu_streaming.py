@@ -203,6 +203,61 @@ def test_swiglu_backward_special_values():
     assert not np.any(diff & ~amb), f"{int((diff & ~amb).sum())} bf16 values differ"
 
 
+def _g_sweep(I):
+    """Every 257th float32 bit pattern that is finite, both signs: ~16.7M gate
+    values over the whole float32 range, in rows of 2I (up values 1)."""
+    bits = np.arange(0, 1 << 32, 257, dtype=np.uint64).astype(np.uint32)
+    g = bits.view(np.float32)
+    g = g[np.isfinite(g)]
+    R = -(-g.size // I)
+    gu = np.ones((R, 2 * I), np.float32)
+    gu[:, :I].reshape(-1)[:g.size] = g
+    gu[:, :I].reshape(-1)[g.size:] = 0.0
+    return gu
+
+
+def test_swiglu_quantize_gate_sweep():
+    """The float64 SwiGLU over the whole float32 range of g (its own exp and
+    reciprocal against numpy's exp and division): h bit for bit off float32
+    midpoints, and every row's bytes equal the oracle's quantiser of the GPU's h."""
+    I = 4096
+    gu = _g_sweep(I)
+    R = gu.shape[0]
+    off = np.array([0, R], np.int32)
+    codes, bsc, rsc, h = pmg.swiglu_quantize(dev(gu), dev(off), h_out=True)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore"):
+        h64 = osw.swiglu_h64(gu)
+    rh = h64.astype(np.float32)
+    amb = osw.rn32_ambiguous(h64)
+    gh = host(h)
+    same = gh.view(np.uint32) == rh.view(np.uint32)
+    print(f"  {R * I} gate values, midpoint-adjacent: {int(amb.sum())}")
+    assert np.all(same | amb), f"h differs at {np.argwhere(~(same | amb))[:5].tolist()}"
+    oc_, ob_, os_ = oq.quantize_rows_f32(gh)
+    assert np.array_equal(host(codes), oc_) and np.array_equal(host(bsc), ob_)
+    assert np.array_equal(host(rsc).view(np.uint32), os_.view(np.uint32))
+
+
+def test_swiglu_backward_gate_sweep():
+    """dG and dU over the whole float32 range of g (dh = 1): bit for bit off bf16 midpoints."""
+    I = 4096
+    gu = _g_sweep(I)
+    R = gu.shape[0]
+    off = np.array([0, R], np.int32)
+    dh = np.ones((R, I), np.float32)
+    dgu = pmg.swiglu_backward(dev(gu), dev(dh), dev(off))
+    torch.cuda.synchronize()
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref_bits, d64 = osw.swiglu_backward_ref(gu, dh)
+        amb = _bf16_midpoint_adjacent(d64)
+    got = bf16_host(dgu)
+    nan_ref = np.isnan(d64)
+    print(f"  {R * I} gate values, midpoint-adjacent: {int(amb.sum())}, NaN: {int(nan_ref.sum())}")
+    diff = (got != ref_bits) & ~nan_ref
+    assert not np.any(diff & ~amb), f"{int((diff & ~amb).sum())} bf16 values differ"
+
+
 @pytest.mark.parametrize("layout", [pmg.W_KN, pmg.W_NK])
 @pytest.mark.parametrize("T,E,k,K,N,kind", [(256, 8, 4, 256, 192, "uniform"),
                                              (40, 16, 2, 96, 64, "zipf"),
