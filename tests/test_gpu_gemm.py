@@ -63,6 +63,7 @@ def _routed_case(T, H, E, k, N, kind, seed):
     (33, 384, 128, 8, 64, "zipf"),         # empty experts, 1-row experts
     (100, 64, 8, 4, 96, "uniform"),        # K = 64: one K-step per tile
     (2000, 64, 64, 8, 512, "zipf"),        # one K-step per tile, several tiles per workgroup
+    (256, 128, 1024, 8, 64, "uniform"),    # the most experts: the prologue's tables over 1024 experts
 ])
 def test_grouped_gemm_small_all_elements(T, H, E, k, N, kind):
     print(f"[gemm] T={T} H={H} E={E} k={k} N={N} {kind}", flush=True)

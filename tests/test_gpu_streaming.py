@@ -261,7 +261,8 @@ def test_swiglu_backward_gate_sweep():
 @pytest.mark.parametrize("layout", [pmg.W_KN, pmg.W_NK])
 @pytest.mark.parametrize("T,E,k,K,N,kind", [(256, 8, 4, 256, 192, "uniform"),
                                              (40, 16, 2, 96, 64, "zipf"),
-                                             (64, 4, 2, 32, 64, "uniform")])   # K = 32: one K-step
+                                             (64, 4, 2, 32, 64, "uniform"),   # K = 32: one K-step
+                                             (256, 1024, 8, 64, 48, "zipf")])  # the most experts
 def test_bf16_grouped_gemm_small(layout, T, E, k, K, N, kind):
     print(f"[bf16 gemm] layout={layout} T={T} E={E} K={K} N={N}", flush=True)
     ids, tw, off, r2t, t2r = _routing(T, E, k, kind, 63)
