@@ -29,6 +29,7 @@ pytestmark = [pytest.mark.gpu,
     (4096, 2048, 128, 8, 768, "zipf", True),
     (300, 256, 16, 4, 256, "uniform", False),       # one h tile, ragged experts, no router weight
     (37, 512, 8, 2, 512, "zipf", True),             # tiny experts, K = 512
+    (256, 256, 1024, 8, 256, "uniform", True),      # the most experts
 ])
 def test_fused_gate_up_swiglu(T, H, E, k, I, kind, weighted):
     print(f"[fused swiglu] T={T} H={H} E={E} k={k} I={I} {kind} weighted={weighted}", flush=True)

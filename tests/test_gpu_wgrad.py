@@ -113,6 +113,23 @@ def _sample(counts):
     return sorted(set([int(np.argmax(counts)), int(np.argmin(counts))] + [int(e) for e in rng.choice(counts.size, 3)]))
 
 
+def test_wgrad_most_experts():
+    """1024 experts (the library's limit), 1024 routed rows: most experts hold 0-2 tokens in their
+    64-token slab; a sample of experts (with the largest and an empty one) against the oracle."""
+    print("[wgrad] E=1024", flush=True)
+    T, E, k = 128, 1024, 8
+    dy = W.gaussian_bf16((T, 256), 1.0, 61, 1)
+    h = (W.rng(61, 2).standard_normal((T * k, 256)) * 0.5).astype(np.float32)
+
+    def sample(rows):
+        picks = set(range(0, E, 37)) | {int(np.argmax(rows))}
+        empty = np.flatnonzero(rows == 0)
+        if empty.size:
+            picks.add(int(empty[0]))
+        return sorted(picks)
+    _run(("token", dy), ("grouped", h), T, E, k, "uniform", 61, sample=sample)
+
+
 @pytest.mark.parametrize("which", ["down", "gate_up"])
 def test_wgrad_layer_sampled(which):
     S = W.LayerShape()
