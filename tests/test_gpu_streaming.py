@@ -42,7 +42,8 @@ def _gu(R, I, seed, scale=2.0):
                                                # rows per wavefront), of two chunks without it
                                                # (lanes past the row end; a whole last chunk)
                                                (2048, 16, 4, 384, True), (300, 8, 4, 1008, False),
-                                               (512, 8, 2, 1024, True)])
+                                               (512, 8, 2, 1024, True),
+                                               (64, 4, 2, 8192, True)])   # the longest row
 def test_swiglu_quantize(T, E, k, I, weighted):
     print(f"[swiglu_quantize] T={T} E={E} k={k} I={I} weighted={weighted}", flush=True)
     ids, tw, off, r2t, t2r = _routing(T, E, k, "uniform", 50)
@@ -114,7 +115,8 @@ def test_permute_gather():
     assert np.array_equal(bf16_host(out), oc.permute_gather_ref(x, r2t, k))
 
 
-@pytest.mark.parametrize("T,E,k,I,weighted", [(4096, 128, 8, 768, True), (40, 4, 2, 24, False)])
+@pytest.mark.parametrize("T,E,k,I,weighted", [(4096, 128, 8, 768, True), (40, 4, 2, 24, False),
+                                               (64, 4, 2, 8192, True)])   # the longest row
 def test_swiglu_backward(T, E, k, I, weighted):
     print(f"[swiglu_backward] T={T} I={I}", flush=True)
     ids, tw, off, r2t, t2r = _routing(T, E, k, "uniform", 62)
