@@ -89,7 +89,9 @@ def test_swiglu_quantize_skips_rows_past_offsets():
                                                    (300, 32, 5, 1024, True, True),  # groups of 4 slots
                                                    (100, 16, 3, 4096, True, False), # one slot at a time
                                                    (37, 16, 4, 264, True, False),   # other H: column loop
-                                                   (20, 8, 3, 64, True, True)])
+                                                   (20, 8, 3, 64, True, True),
+                                                   (64, 64, 32, 2048, True, True),  # top-32, the most slots
+                                                   (16, 64, 32, 8200, True, False)])  # long rows, column loop
 def test_unpermute_combine(T, E, k, H, weighted, bad):
     print(f"[combine] T={T} k={k} H={H} weighted={weighted} invalid={bad}", flush=True)
     ids, tw, _, _, _ = _routing(T, E, k, "uniform", 60)
