@@ -107,10 +107,12 @@ def test_unpermute_combine(T, E, k, H, weighted, bad):
     assert np.array_equal(bf16_host(y), ry)
 
 
-def test_permute_gather():
-    print("[gather]", flush=True)
-    T, E, k, H = 4096, 128, 8, 2048
-    ids, tw, off, r2t, t2r = _routing(T, E, k, "softmax", 61)
+@pytest.mark.parametrize("T,E,k,H,kind", [(4096, 128, 8, 2048, "softmax"),
+                                          (64, 64, 32, 264, "zipf"),      # top-32, short odd-width rows
+                                          (50, 16, 3, 8192, "uniform")])  # the longest rows
+def test_permute_gather(T, E, k, H, kind):
+    print(f"[gather] T={T} E={E} k={k} H={H}", flush=True)
+    ids, tw, off, r2t, t2r = _routing(T, E, k, kind, 61)
     x = W.gaussian_bf16((T, H), 1.0, 61, 32)
     out = pmg.permute_gather_bf16(bf16_dev(x), dev(off), dev(r2t), k)
     torch.cuda.synchronize()
