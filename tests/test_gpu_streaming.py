@@ -302,7 +302,8 @@ def test_bf16_dgrad_shapes_sampled(K, N, kind):
 
 
 @pytest.mark.parametrize("T,E,k,K,N,kind", [(4096, 128, 8, 2048, 768, "softmax"),
-                                             (40, 16, 2, 96, 64, "zipf")])
+                                             (40, 16, 2, 96, 64, "zipf"),
+                                             (64, 64, 32, 128, 96, "uniform")])   # top-32: row r / 32
 def test_bf16_grouped_gemm_gather(T, E, k, K, N, kind):
     """The gathered-operand GEMM equals the GEMM of the gathered rows bit for bit, and the oracle."""
     print(f"[bf16 gemm gather] T={T} E={E} k={k} K={K} N={N} {kind}", flush=True)
