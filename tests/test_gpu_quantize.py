@@ -77,6 +77,63 @@ def test_quantize_rows_edge_values():
     _check_rows(W.f32_to_bf16_bits(worked[None]), "worked example")
 
 
+def _check_rows_f32(x, tag):
+    print(f"[quantize_rows_f32] {tag} shape={x.shape}", flush=True)
+    got = pmg.nvfp4_quantize_rows_f32(dev(x))
+    torch.cuda.synchronize()
+    for g, r, name in zip(got, oq.quantize_rows_f32(x), ("codes", "bscales", "rscales")):
+        g = host(g)
+        if name == "rscales":
+            assert np.array_equal(g.view(np.uint32), r.view(np.uint32)), f"{tag}: {name}"
+        else:
+            bad = np.argwhere(g != r)
+            assert bad.size == 0, f"{tag}: {name} differs at {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("K", [16, 48, 256, 528, 768, 1024, 2048, 4096, 8192])
+def test_quantize_rows_f32_lengths(K):
+    """FP32 rows with full 24-bit significands (the fused SwiGLU path's h) of every row kernel's length."""
+    x = (W.rng(4, K).standard_normal((37, K)) * 3.0).astype(np.float32)
+    x[::5, K // 3] *= 50.0                                                  # outliers
+    _check_rows_f32(x, f"K={K}")
+
+
+def test_quantize_rows_f32_edge_values():
+    rng = np.random.default_rng(8)
+    rows = [np.zeros(64, np.float32)]                                       # zero row
+    z = np.zeros(64, np.float32); z[::3] = -0.0; rows.append(z)             # signed zeros
+    t = np.zeros(64, np.float32); t[0] = 1e-30; t[16:32] = 1.1e-35; t[32:] = -1e-38
+    rows.append(t)                                                          # tiny and zero block scales
+    rows.append(np.full(64, 3.4e38, np.float32))                            # near the float32 maximum
+    rows.append(np.full(64, -1.4e-45, np.float32))                          # the least float32 subnormal
+    sub = (rng.standard_normal(64) * 1e-40).astype(np.float32); rows.append(sub)   # float32 subnormals
+    one = np.zeros(64, np.float32); one[37] = np.float32(0.1); rows.append(one)    # a single nonzero
+    r = rng.standard_normal(64).astype(np.float32); r[5] = 1e6; rows.append(r)
+    ties = (np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 8) * 1.875 * 2.0 ** -8).astype(np.float32)
+    ties[::16] = 11.25 * 2.0 ** -8
+    ties[0] = 10.5
+    rows.append(ties)                                                       # E2M1 midpoints
+    near = ties.copy()
+    near[1::2] = np.nextafter(near[1::2], np.float32(np.inf))               # one float32 ulp above them
+    rows.append(near)
+    _check_rows_f32(np.stack(rows), "edge values")
+
+
+def test_quantize_rows_f32_routed_rows_only():
+    """With expert offsets, rows from offsets[E] on are not written."""
+    x = (W.rng(5, 1).standard_normal((40, 768)) * 2.0).astype(np.float32)
+    off = np.array([0, 10, 10, 29], np.int32)
+    codes = torch.full((40, 384), 0xAB, dtype=torch.uint8, device="cuda:0")
+    bsc = torch.full((40, 48), 0xCD, dtype=torch.uint8, device="cuda:0")
+    rsc = torch.full((40,), -7.0, dtype=torch.float32, device="cuda:0")
+    pmg.nvfp4_quantize_rows_f32(dev(x), dev(off), codes, bsc, rsc)
+    torch.cuda.synchronize()
+    rc, rb, rs = oq.quantize_rows_f32(x[:29])
+    assert np.array_equal(host(codes)[:29], rc) and np.array_equal(host(bsc)[:29], rb)
+    assert np.array_equal(host(rsc)[:29].view(np.uint32), rs.view(np.uint32))
+    assert np.all(host(codes)[29:] == 0xAB) and np.all(host(bsc)[29:] == 0xCD) and np.all(host(rsc)[29:] == -7.0)
+
+
 def test_quantize_rows_e2m1_encode_sweep():
     """Every bf16 value of magnitude up to 6, both signs, as an exact quotient
     x / d: the row amax 2688 makes s = 1, and every other block holds a +-6, so
